@@ -1,0 +1,51 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+Holds none of the attention arithmetic: it only draws iid N(0,1) tensors from
+fixed seeds (torch Philox on a GPU, torch's CPU generator on the host), casts
+them to the compute dtype, and picks seeded row samples.  Both the oracle side
+and the HIP side receive the very same cast values.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+SEED_Q, SEED_K, SEED_V = 1000, 1001, 1002
+
+
+def _randn(shape, seed: int, device, dtype) -> torch.Tensor:
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+def make_qkv(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, *,
+             dtype=torch.bfloat16, device="cpu", seeds=(SEED_Q, SEED_K, SEED_V),
+             high_freq_scale: float | None = None):
+    """q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d], iid N(0,1) drawn in fp32 then cast.
+
+    ``high_freq_scale``: if set, the first half of the rotary pairs (the fast
+    ones, dims [0, d/4) and [d/2, 3d/4)) of q and k is multiplied by this
+    factor before the cast, so that the distance windows change the output a
+    lot (a structured input for discrimination checks).
+    """
+    q = _randn((B, Hq, Sq, d), seeds[0], device, torch.float32)
+    k = _randn((B, Hkv, Sk, d), seeds[1], device, torch.float32)
+    v = _randn((B, Hkv, Sk, d), seeds[2], device, torch.float32)
+    if high_freq_scale is not None:
+        half, quarter = d // 2, d // 4
+        for t in (q, k):
+            t[..., :quarter] *= high_freq_scale
+            t[..., half:half + quarter] *= high_freq_scale
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def sample_rows(S: int, n: int, seed: int = 7) -> np.ndarray:
+    """n distinct query indices in [0, S): always 0 and S-1, the rest seeded uniform."""
+    n = min(n, S)
+    rng = np.random.default_rng(seed)
+    picked = {0, S - 1}
+    while len(picked) < n:
+        picked.add(int(rng.integers(0, S)))
+    return np.array(sorted(picked), dtype=np.int64)[:max(n, 1)]
