@@ -1,0 +1,153 @@
+/*
+ * atf.h -- C ABI of librfw_atf.so: causal attention with per-RoPE-wavelength
+ * distance windows (the ATFlash idea) for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Source page: "ATFlash: RoPE-Frequenzen kuerzen
+ * Attention-Arbeit um bis zu 57 Prozent" (sudo-ai.de).
+ *   Section "Was ATFlash anders macht": RoPE rotates each pair of head dims at
+ *   its own frequency; each pair gets a distance window derived from its
+ *   wavelength, beyond which that pair's share of the query-key product is
+ *   left out; slow pairs keep distant keys reachable (unlike a sliding window).
+ *   Section "Die Zahlen - und ihre Grenze": prefill and decode attention keep
+ *   their online-softmax recurrence unchanged.
+ *   Readings used where the page gives no formula:
+ *     P = d/2 pairs, pair p = head dims (p, p + P) (half-split layout),
+ *     theta_p = rope_base^(-2p/d), lambda_p = 2*pi/theta_p,
+ *     W_p = ceil(alpha * lambda_p) for p < P-1, W_{P-1} = infinity,
+ *     rotation by +angle (pos * theta_p):
+ *       x'_p = x_p cos - x_{p+P} sin,  x'_{p+P} = x_{p+P} cos + x_p sin,
+ *     score(i,j) = sum over p with (pos_i - pos_j) <= W_p of
+ *                  q'_p k'_p + q'_{p+P} k'_{p+P},
+ *     out_i = softmax_j(score(i,j) / sqrt(d)) . v_j over keys j with pos_j <= pos_i.
+ *
+ * Conventions shared by every call.
+ *   - Tensors are DEVICE pointers owned by the caller, densely packed, 16-byte
+ *     aligned:  q, out [B][Hq][Sq][d];  k, v [B][Hkv][S][d].
+ *     q and k are given BEFORE the rotary embedding; the library rotates them.
+ *   - GQA: query head h reads key/value head h / (Hq / Hkv).
+ *   - dtype is the element type of q, k, v and out (fp32 accumulation always).
+ *   - Positions: key j sits at pos0 + j.  Prefill query i sits at pos0 + i;
+ *     the decode query sits at pos0 + S (right after the S cached keys).
+ *   - All work is queued on `stream` (hipStream_t; NULL = default stream) and
+ *     is asynchronous, except that a non-NULL skipped_out makes the call wait
+ *     for the stream and copy the count back.
+ *   - The library never allocates device memory inside a call: scratch space
+ *     is the caller's `workspace` (size from the *_workspace_bytes query).
+ *   - Errors are status codes only; nothing throws or aborts.  Every argument
+ *     check runs on the host before anything is queued.
+ *   - Supported: d in {64, 128}; Hq % Hkv == 0; Hq/Hkv <= 64; S >= 1;
+ *     0 <= pos0 and pos0 + S + 1 < 2^31; alpha > 0 (finite or +inf; +inf
+ *     means no window); rope_base > 1 and finite; causal == 1 (0 returns
+ *     ATF_ERR_UNSUPPORTED).
+ */
+#ifndef ATF_H
+#define ATF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *atf_stream_t; /* same object as hipStream_t */
+
+typedef enum {
+    ATF_OK = 0,
+    ATF_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value */
+    ATF_ERR_UNSUPPORTED = 2, /* valid but not implemented (d, causal=0, ...) */
+    ATF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    ATF_ERR_HIP = 4          /* a HIP launch or copy failed */
+} atf_status;
+
+typedef enum { ATF_F32 = 0, ATF_BF16 = 1 } atf_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *atf_status_string(atf_status s);
+
+/* Library version string (static). */
+const char *atf_version(void);
+
+/*
+ * Window table: W_out[p] for p < d/2, computed in fp64 on the host.
+ * INT64_MAX marks an uncut pair (always the slowest pair, every pair when
+ * alpha is +inf).  Any even d >= 2 is accepted here.
+ */
+atf_status atf_window_table(int32_t d, double rope_base, double alpha, int64_t *W_out);
+
+/*
+ * Closed-form number of dropped (query, key, pair) terms for ONE (batch,
+ * query-head) pair:  causal prefill of S tokens (is_decode = 0):
+ * sum_p n_p (n_p + 1) / 2 with n_p = max(0, S - 1 - W_p);  decode of one query
+ * after S keys (is_decode = 1): sum_p max(0, S - W_p).  causal must be 1.
+ */
+atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, double alpha,
+                                     int32_t causal, int32_t is_decode, uint64_t *per_head_out);
+
+/* ------------------------------------------------------------------ prefill */
+
+/* Bytes of workspace atf_prefill needs (rotated keys, re-laid-out values,
+ * counters).  Returns 0 for unsupported shapes. */
+size_t atf_prefill_workspace_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype dtype);
+
+/*
+ * Causal windowed-RoPE prefill attention over S tokens:  out = attention(q, k, v).
+ * Equivalent to atf_prefill_prepare_kv followed by atf_prefill_attend.
+ * skipped_out (HOST pointer, nullable): receives the number of dropped
+ * (query, key, pair) terms summed over all B*Hq heads, as counted by the
+ * kernels; setting it synchronises `stream`.
+ */
+atf_status atf_prefill(const void *q, const void *k, const void *v, void *out,
+                       int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
+                       double rope_base, double alpha, int32_t causal, int64_t pos0,
+                       atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                       uint64_t *skipped_out, atf_stream_t stream);
+
+/*
+ * First half of atf_prefill: rotates every key at pos0 + j once and stores it
+ * in `workspace` in the layout the attention kernel reads (bf16: rotated keys
+ * with each pair's two dims side by side, values transposed per 64-key tile),
+ * and clears the skipped-term counter (fp32: only clears the counter; the
+ * fp32 kernel rotates keys as it streams them).
+ */
+atf_status atf_prefill_prepare_kv(const void *k, const void *v,
+                                  int32_t B, int32_t Hkv, int64_t S, int32_t d,
+                                  double rope_base, int64_t pos0, atf_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, atf_stream_t stream);
+
+/*
+ * Second half of atf_prefill: the attention kernel itself, reading q plus the
+ * workspace prepared by atf_prefill_prepare_kv with the same B, Hkv, S, d,
+ * rope_base, pos0 and dtype.  k and v are the raw inputs: the fp32 kernel
+ * reads (and rotates) them directly; the bf16 kernel ignores them (NULL ok).
+ */
+atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void *out,
+                              int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
+                              double rope_base, double alpha, int32_t causal, int64_t pos0,
+                              atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                              uint64_t *skipped_out, atf_stream_t stream);
+
+/* ------------------------------------------------------------------- decode */
+
+/* Bytes of workspace atf_decode needs (per-split partial results + counter). */
+size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d);
+
+/*
+ * Windowed-RoPE decode: one new query per sequence, at position pos0 + S,
+ * attending to the S cached keys at pos0 .. pos0 + S - 1.
+ *   q, out [B][Hq][1][d];  k, v [B][Hkv][S][d] (the cache, pre-RoPE keys).
+ * bf16 runs the split-KV kernel (each split reads only the key dims still
+ * inside their window) followed by a combine kernel; fp32 runs a plain
+ * per-query kernel.  skipped_out as for atf_prefill.
+ */
+atf_status atf_decode(const void *q, const void *k, const void *v, void *out,
+                      int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
+                      double rope_base, double alpha, int32_t causal, int64_t pos0,
+                      atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                      uint64_t *skipped_out, atf_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATF_H */

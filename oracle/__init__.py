@@ -57,7 +57,7 @@ def _bind(path: str):
     lib.orc_attention_rows.argtypes = [
         f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
-        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, i64p, ctypes.c_int64, f64p, u64p]
+        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, i64p, ctypes.c_int64, f32p, f64p, u64p]
     lib.orc_attention_rows.restype = ctypes.c_int
     lib.orc_skipped_closed_form.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int, u64p]
@@ -109,17 +109,22 @@ class Oracle:
         return np.ascontiguousarray(x, dtype=np.float32)
 
     def attention(self, q, k, v, *, base: float, alpha: float, causal: bool = True,
-                  q_pos0: int = 0, k_pos0: int = 0, rows=None):
+                  q_pos0: int = 0, k_pos0: int = 0, rows=None, q_shape=None):
         """Windowed-RoPE attention in fp64.
 
         q: [B, Hq, Sq, d]; k, v: [B, Hkv, Sk, d] (any float dtype; values are used
         exactly).  Query i sits at ``q_pos0 + i``, key j at ``k_pos0 + j``.
         ``rows``: optional int array [n, 3] of (b, h_q, i); default all rows.
+        ``q_shape``: if given as (B, Hq, Sq, d), ``q`` holds only the listed
+        rows' query vectors, [n, d] (for sampled rows of huge inputs).
         Returns (out, skipped): out is [n, d] fp64 when ``rows`` is given, else
         [B, Hq, Sq, d]; skipped is the number of dropped (row, key, pair) terms.
         """
         q32, k32, v32 = self._as_f32(q), self._as_f32(k), self._as_f32(v)
-        B, Hq, Sq, d = q32.shape
+        compact = q_shape is not None
+        if compact and rows is None:
+            raise ValueError("compact query rows need `rows`")
+        B, Hq, Sq, d = q_shape if compact else q32.shape
         Bk, Hkv, Sk, dk = k32.shape
         if Bk != B or dk != d or v32.shape != k32.shape:
             raise ValueError("shape mismatch")
@@ -131,11 +136,15 @@ class Oracle:
         out = np.zeros((rows.shape[0], d), dtype=np.float64)
         skipped = ctypes.c_uint64(0)
         f32p = ctypes.POINTER(ctypes.c_float)
+        if compact and q32.shape != (rows.shape[0], d):
+            raise ValueError("compact q must be [n_rows, d]")
         rc = self.lib.orc_attention_rows(
-            q32.ctypes.data_as(f32p), k32.ctypes.data_as(f32p), v32.ctypes.data_as(f32p),
+            None if compact else q32.ctypes.data_as(f32p), k32.ctypes.data_as(f32p),
+            v32.ctypes.data_as(f32p),
             B, Hq, Hkv, Sq, Sk, d, float(base), float(alpha), 1 if causal else 0,
             int(q_pos0), int(k_pos0),
             rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.shape[0],
+            q32.ctypes.data_as(f32p) if compact else None,
             out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ctypes.byref(skipped))
         if rc != 0:
             raise ValueError("bad oracle arguments")

@@ -97,6 +97,9 @@ static void orc_rotate(const float *x, int d, double pos, const double *theta, d
  *   query i sits at position q_pos0 + i, key j at k_pos0 + j,
  *   delta = (q_pos0 + i) - (k_pos0 + j).  causal: only keys with delta >= 0.
  *   rows: n_rows triples (b, h_q, i); out: [n_rows][d] fp64.
+ *   q_rows (nullable): if given, row r's query vector is q_rows[r][0..d)
+ *       instead of q[b][h_q][i] (lets a caller pass only sampled rows);
+ *       q may then be NULL.
  *   GQA: query head h reads key/value head h / (Hq / Hkv).
  *   skipped (nullable): number of (row, key, pair) terms left out, summed
  *   over the listed rows (causal keys only when causal != 0).
@@ -106,12 +109,14 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
                        int B, int Hq, int Hkv, int64_t Sq, int64_t Sk, int d,
                        double base, double alpha, int causal,
                        int64_t q_pos0, int64_t k_pos0,
-                       const int64_t *rows, int64_t n_rows,
+                       const int64_t *rows, int64_t n_rows, const float *q_rows,
                        double *out, uint64_t *skipped)
 {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || (Hq % Hkv) != 0 || Sq <= 0 || Sk <= 0)
         return -1;
     if (d <= 0 || (d % 2) != 0 || rows == NULL || out == NULL || n_rows < 0)
+        return -1;
+    if (q == NULL && q_rows == NULL)
         return -1;
     const int P = d / 2;
     const int group = Hq / Hkv;
@@ -171,7 +176,8 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
                     if (rows[3 * r] != b || rows[3 * r + 1] / group != hk)
                         continue;
                     int64_t h = rows[3 * r + 1], i = rows[3 * r + 2];
-                    const float *qrow = q + (((size_t)b * Hq + h) * (size_t)Sq + i) * d;
+                    const float *qrow = q_rows ? q_rows + (size_t)r * d
+                                               : q + (((size_t)b * Hq + h) * (size_t)Sq + i) * d;
                     int64_t qpos = q_pos0 + i;
                     orc_rotate(qrow, d, (double)qpos, theta, qrot);
 

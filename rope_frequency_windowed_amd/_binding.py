@@ -1,0 +1,228 @@
+"""ctypes binding over librfw_atf.so (include/atf.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, torch's current
+HIP stream becomes the call's stream, and torch allocates the caller-owned
+workspace.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind -- if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librfw_atf.so")
+
+ATF_OK, ATF_ERR_INVALID_ARG, ATF_ERR_UNSUPPORTED, ATF_ERR_WORKSPACE, ATF_ERR_HIP = range(5)
+ATF_F32, ATF_BF16 = 0, 1
+W_INF = np.iinfo(np.int64).max
+
+# every symbol include/atf.h declares
+EXPORTED = (
+    "atf_status_string", "atf_version", "atf_window_table", "atf_skipped_pair_products",
+    "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
+    "atf_prefill_attend", "atf_decode_workspace_bytes", "atf_decode",
+)
+
+
+class AtfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, _lib().atf_status_string(status).decode()))
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("librfw_atf.so is not built (expected at %s); run "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.atf_status_string.argtypes = [ctypes.c_int]
+    lib.atf_status_string.restype = ctypes.c_char_p
+    lib.atf_version.argtypes = []
+    lib.atf_version.restype = ctypes.c_char_p
+    lib.atf_window_table.argtypes = [i32, f64, f64, i64p]
+    lib.atf_window_table.restype = ctypes.c_int
+    lib.atf_skipped_pair_products.argtypes = [i64, i32, f64, f64, i32, i32, u64p]
+    lib.atf_skipped_pair_products.restype = ctypes.c_int
+    lib.atf_prefill_workspace_bytes.argtypes = [i32, i32, i64, i32, ctypes.c_int]
+    lib.atf_prefill_workspace_bytes.restype = sz
+    lib.atf_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+                                ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_prefill.restype = ctypes.c_int
+    lib.atf_prefill_prepare_kv.argtypes = [vp, vp, i32, i32, i64, i32, f64, i64, ctypes.c_int,
+                                           vp, sz, vp]
+    lib.atf_prefill_prepare_kv.restype = ctypes.c_int
+    lib.atf_prefill_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+                                       ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_prefill_attend.restype = ctypes.c_int
+    lib.atf_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+    lib.atf_decode_workspace_bytes.restype = sz
+    lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+                               ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_decode.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def _check(status: int, where: str):
+    if status != ATF_OK:
+        raise AtfError(status, where)
+
+
+# ------------------------------------------------------------- host-only calls
+
+def atf_version() -> str:
+    return _lib().atf_version().decode()
+
+
+def atf_window_table(d: int, rope_base: float, alpha: float) -> np.ndarray:
+    W = np.zeros(max(d // 2, 1), dtype=np.int64)
+    _check(_lib().atf_window_table(d, rope_base, alpha, W.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+           "atf_window_table")
+    return W[: d // 2]
+
+
+def atf_skipped_pair_products(S: int, d: int, rope_base: float, alpha: float, causal: int = 1,
+                              is_decode: int = 0) -> int:
+    out = ctypes.c_uint64(0)
+    _check(_lib().atf_skipped_pair_products(S, d, rope_base, alpha, causal, is_decode, ctypes.byref(out)),
+           "atf_skipped_pair_products")
+    return int(out.value)
+
+
+def atf_prefill_workspace_bytes(B: int, Hkv: int, S: int, d: int, dtype: int) -> int:
+    return int(_lib().atf_prefill_workspace_bytes(B, Hkv, S, d, dtype))
+
+
+def atf_decode_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
+    return int(_lib().atf_decode_workspace_bytes(B, Hq, Hkv, S, d))
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATF_BF16
+    if t.dtype == torch.float32:
+        return ATF_F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device, tag: str):
+    """A cached caller-owned workspace of at least nbytes on `device`."""
+    torch = _torch()
+    key = (str(device), tag)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def atf_prefill(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
+                ws=None, return_skipped: bool = False):
+    """Causal windowed-RoPE prefill.  q [B,Hq,S,d], k/v [B,Hkv,S,d] (pre-RoPE)."""
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    nbytes = atf_prefill_workspace_bytes(B, Hkv, S, d, code)
+    if ws is None:
+        ws = workspace(nbytes, q.device, "prefill")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                              B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal), int(pos0),
+                              code, _dev(ws, "workspace"), ws.numel(),
+                              ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_prefill")
+    return (out, int(skipped.value)) if return_skipped else out
+
+
+def atf_prefill_prepare_kv(k, v, *, rope_base: float, pos0: int = 0, ws):
+    B, Hkv, S, d = k.shape
+    code = _dtype_code(k)
+    _check(_lib().atf_prefill_prepare_kv(_dev(k, "k"), _dev(v, "v"), B, Hkv, S, d, float(rope_base),
+                                         int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                         _stream(k.device)),
+           "atf_prefill_prepare_kv")
+
+
+def atf_prefill_attend(q, k, v, out, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
+                       ws, return_skipped: bool = False):
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_prefill_attend(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                     B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal),
+                                     int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                     ctypes.byref(skipped) if return_skipped else None,
+                                     _stream(q.device)),
+           "atf_prefill_attend")
+    return int(skipped.value) if return_skipped else None
+
+
+def atf_decode(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
+               ws=None, return_skipped: bool = False):
+    """Windowed-RoPE decode: q [B,Hq,1,d] at position pos0+S over the cache k/v [B,Hkv,S,d]."""
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence")
+    Hkv, S = k.shape[1], k.shape[2]
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    nbytes = atf_decode_workspace_bytes(B, Hq, Hkv, S, d)
+    if ws is None:
+        ws = workspace(nbytes, q.device, "decode")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_decode(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                             B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal), int(pos0),
+                             code, _dev(ws, "workspace"), ws.numel(),
+                             ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_decode")
+    return (out, int(skipped.value)) if return_skipped else out
+
+
+ALPHA_INF = math.inf

@@ -1,0 +1,370 @@
+// Host side of librfw_atf.so: argument checks, the fp64 window table, the
+// closed-form dropped-term count, the decode split planner and the C entry
+// points declared in include/atf.h.
+//
+// Method: source page "ATFlash: RoPE-Frequenzen kuerzen Attention-Arbeit um
+// bis zu 57 Prozent" (sudo-ai.de), section "Was ATFlash anders macht" (each
+// rotary pair is cut beyond a distance proportional to its wavelength, the
+// slow pairs keep far keys reachable) and section "Die Zahlen - und ihre
+// Grenze" (prefill and decode keep the online softmax unchanged).
+
+#include "../../include/atf.h"
+#include "atf_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+using namespace atf;
+
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr int64_t kInf64 = INT64_MAX;
+constexpr size_t kHeaderBytes = 256;  // workspace head: the dropped-term counter
+
+// W_p = ceil(alpha * lambda_p), lambda_p = 2 pi base^(2p/d); the slowest pair
+// and every pair at alpha = inf are uncut.  fp64 throughout: alpha*lambda_p
+// sits at least ~3e-3 from an integer at every benchmarked setting, far
+// beyond fp64 rounding, so the ceiling is stable.
+void window_table(int d, double base, double alpha, int64_t *W) {
+    const int P = d / 2;
+    const double log_base = std::log(base);
+    for (int p = 0; p < P; ++p) {
+        if (p == P - 1 || std::isinf(alpha)) {
+            W[p] = kInf64;
+            continue;
+        }
+        const double lambda = kTwoPi * std::exp(log_base * (2.0 * p / d));
+        const double x = std::ceil(alpha * lambda);
+        W[p] = (x >= 9.0e18) ? kInf64 : (int64_t)x;
+    }
+}
+
+// rotary angle step of pair p: base^(-2p/d)
+void theta_table(int d, double base, double *theta) {
+    const int P = d / 2;
+    const double log_base = std::log(base);
+    for (int p = 0; p < kMaxPairs; ++p) theta[p] = (p < P) ? std::exp(-log_base * (2.0 * p / d)) : 0.0;
+}
+
+// Windows as the kernels see them: int32, kWindowInf for "never cut".  Every
+// distance a kernel meets is < 2^31 - 1, so clamping changes no decision.
+void window_table_i32(int d, double base, double alpha, int *Wi) {
+    int64_t W[kMaxPairs];
+    window_table(d, base, alpha, W);
+    for (int p = 0; p < kMaxPairs; ++p) {
+        if (p >= d / 2 || W[p] >= (int64_t)kWindowInf) Wi[p] = kWindowInf;
+        else Wi[p] = (int)W[p];
+    }
+}
+
+bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+atf_status check_shape(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double base,
+                       double alpha, int32_t causal, int64_t pos0, atf_dtype dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1) return ATF_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return ATF_ERR_INVALID_ARG;
+    if (d < 2 || (d & 1)) return ATF_ERR_INVALID_ARG;
+    if (!std::isfinite(base) || !(base > 1.0)) return ATF_ERR_INVALID_ARG;
+    if (std::isnan(alpha) || !(alpha > 0.0)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return ATF_ERR_INVALID_ARG;
+    if (pos0 < 0 || pos0 + S + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 64) return ATF_ERR_UNSUPPORTED;
+    if (causal == 0) return ATF_ERR_UNSUPPORTED;
+    return ATF_OK;
+}
+
+size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype dtype) {
+    if (dtype == ATF_F32) return kHeaderBytes;
+    const size_t per = (size_t)B * Hkv * (size_t)padded_keys(S) * d * 2;  // bf16
+    return kHeaderBytes + 2 * per;  // rotated keys + transposed values
+}
+
+// ---------------------------------------------------------------- decode plan
+
+struct DecodePlan {
+    int nsplit = 1;
+    int n_slabs = 1;
+    int starts[kMaxSplits + 1];
+};
+
+int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S) {
+    const int group = Hq / Hkv;
+    const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
+    const int64_t units = (int64_t)B * Hkv * n_slabs;
+    const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
+    // aim for ~2048 workgroups (8 per CU on 256 CUs), at least one chunk each
+    int64_t ns = (2048 + units - 1) / units;
+    ns = std::min<int64_t>(ns, kMaxSplits);
+    ns = std::min<int64_t>(ns, nchunks);
+    return (int)std::max<int64_t>(ns, 1);
+}
+
+size_t decode_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
+    const int ns = decode_nsplit(B, Hq, Hkv, S);
+    return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
+}
+
+// Splits of equal ALGORITHMIC bytes: a key at distance D costs
+// 4 (P - p*(D)) bytes of kept key pairs plus 2d bytes of value, so far chunks
+// (fewer kept pairs) are longer.  Boundaries fall on 64-key chunks.
+void plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, const int *Wi,
+                 DecodePlan &plan) {
+    const int P = d / 2;
+    const int group = Hq / Hkv;
+    plan.n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
+    plan.nsplit = decode_nsplit(B, Hq, Hkv, S);
+    const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
+    std::vector<double> cum((size_t)nchunks + 1, 0.0);
+    for (int64_t c = 0; c < nchunks; ++c) {
+        double bytes = 0.0;
+        const int64_t jend = std::min<int64_t>(S, (c + 1) * kKeyTile);
+        for (int64_t j = c * kKeyTile; j < jend; ++j) {
+            const int64_t delta = S - j;
+            int ps = 0;
+            while (ps < P - 1 && (int64_t)Wi[ps] < delta) ++ps;
+            bytes += 4.0 * (P - ps) + 2.0 * d;
+        }
+        cum[(size_t)c + 1] = cum[(size_t)c] + bytes;
+    }
+    const double total = cum[(size_t)nchunks];
+    plan.starts[0] = 0;
+    int64_t c = 0;
+    for (int s = 1; s < plan.nsplit; ++s) {
+        const double target = total * s / plan.nsplit;
+        while (c < nchunks && cum[(size_t)c] < target) ++c;
+        // keep every split non-empty
+        const int64_t lo = plan.starts[s - 1] / kKeyTile + 1;
+        const int64_t hi = nchunks - (plan.nsplit - s);
+        const int64_t cc = std::max(lo, std::min(c, hi));
+        plan.starts[s] = (int)(cc * kKeyTile);
+    }
+    plan.starts[plan.nsplit] = (int)(nchunks * kKeyTile);
+}
+
+atf_status hip_status(hipError_t e) { return e == hipSuccess ? ATF_OK : ATF_ERR_HIP; }
+
+atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) {
+    if (!host) return ATF_OK;
+    unsigned long long v = 0;
+    if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return ATF_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return ATF_ERR_HIP;
+    *host = (uint64_t)v;
+    return ATF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *atf_status_string(atf_status s) {
+    switch (s) {
+        case ATF_OK: return "ATF_OK";
+        case ATF_ERR_INVALID_ARG: return "ATF_ERR_INVALID_ARG";
+        case ATF_ERR_UNSUPPORTED: return "ATF_ERR_UNSUPPORTED";
+        case ATF_ERR_WORKSPACE: return "ATF_ERR_WORKSPACE";
+        case ATF_ERR_HIP: return "ATF_ERR_HIP";
+    }
+    return "ATF_UNKNOWN_STATUS";
+}
+
+const char *atf_version(void) { return "rfw-atf 0.1 gfx950"; }
+
+atf_status atf_window_table(int32_t d, double rope_base, double alpha, int64_t *W_out) {
+    if (!W_out || d < 2 || (d & 1) || d > 65536) return ATF_ERR_INVALID_ARG;
+    if (!std::isfinite(rope_base) || !(rope_base > 1.0)) return ATF_ERR_INVALID_ARG;
+    if (std::isnan(alpha) || !(alpha > 0.0)) return ATF_ERR_INVALID_ARG;
+    window_table(d, rope_base, alpha, W_out);
+    return ATF_OK;
+}
+
+atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, double alpha,
+                                     int32_t causal, int32_t is_decode, uint64_t *per_head_out) {
+    if (!per_head_out || S < 1 || (is_decode != 0 && is_decode != 1)) return ATF_ERR_INVALID_ARG;
+    if (causal != 1) return causal == 0 ? ATF_ERR_UNSUPPORTED : ATF_ERR_INVALID_ARG;
+    std::vector<int64_t> W((size_t)std::max(1, d / 2));
+    atf_status st = atf_window_table(d, rope_base, alpha, W.data());
+    if (st != ATF_OK) return st;
+    uint64_t total = 0;
+    for (int64_t w : W) {
+        if (w == kInf64) continue;
+        // distances 1..S-1 occur S - t times in prefill; decode sees 1..S once each
+        const int64_t n = is_decode ? S - w : S - 1 - w;
+        if (n <= 0) continue;
+        total += is_decode ? (uint64_t)n : (uint64_t)n * (uint64_t)(n + 1) / 2u;
+    }
+    *per_head_out = total;
+    return ATF_OK;
+}
+
+size_t atf_prefill_workspace_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype dtype) {
+    if (B < 1 || Hkv < 1 || S < 1 || (d != 64 && d != 128)) return 0;
+    if (dtype != ATF_F32 && dtype != ATF_BF16) return 0;
+    return prefill_ws_bytes(B, Hkv, S, d, dtype);
+}
+
+atf_status atf_prefill_prepare_kv(const void *k, const void *v, int32_t B, int32_t Hkv, int64_t S,
+                                  int32_t d, double rope_base, int64_t pos0, atf_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, atf_stream_t stream) {
+    atf_status st = check_shape(B, Hkv, Hkv, S, d, rope_base, 1.0, 1, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!aligned16(k) || !aligned16(v)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    PrepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.v = v;
+    a.counter = (unsigned long long *)workspace;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.S = (int)S;
+    a.S_pad = (int)padded_keys(S);
+    a.pos0 = pos0;
+    theta_table(d, rope_base, a.theta);
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == ATF_F32) return hip_status(launch_prep_f32(a, d, s));
+    char *ws = (char *)workspace + kHeaderBytes;
+    const size_t per = (size_t)B * Hkv * (size_t)a.S_pad * d * 2;
+    a.krot = ws;
+    a.vt = ws + per;
+    return hip_status(launch_prep_bf16(a, d, s));
+}
+
+atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
+                              int32_t Hkv, int64_t S, int32_t d, double rope_base, double alpha,
+                              int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                              size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+    atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.out = out;
+    a.counter = (unsigned long long *)workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.Sq = (int)S;
+    a.Sk = (int)S;
+    a.Sk_pad = (int)padded_keys(S);
+    a.q_pos0 = pos0;
+    a.k_pos0 = pos0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (dtype == ATF_F32) {
+        // the fp32 kernel rotates raw keys itself: `krot` carries k, `vt` carries v
+        a.krot = k;
+        a.vt = v;
+        a.Sk_pad = (int)S;
+        e = launch_attend_f32(a, d, s);
+    } else {
+        char *ws = (char *)workspace + kHeaderBytes;
+        const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
+        a.krot = ws;
+        a.vt = ws + per;
+        a.n_qtiles = (int)((S + kQueryTile - 1) / kQueryTile);
+        a.n_groups = a.n_qtiles * B * Hkv;
+        e = launch_prefill_bf16(a, d, s);
+    }
+    if (e != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(a.counter, skipped_out, s);
+}
+
+atf_status atf_prefill(const void *q, const void *k, const void *v, void *out, int32_t B,
+                       int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double rope_base,
+                       double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
+                       void *workspace, size_t workspace_bytes, uint64_t *skipped_out,
+                       atf_stream_t stream) {
+    atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    st = atf_prefill_prepare_kv(k, v, B, Hkv, S, d, rope_base, pos0, dtype, workspace,
+                                workspace_bytes, stream);
+    if (st != ATF_OK) return st;
+    return atf_prefill_attend(q, k, v, out, B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype,
+                              workspace, workspace_bytes, skipped_out, stream);
+}
+
+size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || (d != 64 && d != 128)) return 0;
+    return decode_ws_bytes(B, Hq, Hkv, S, d);
+}
+
+atf_status atf_decode(const void *q, const void *k, const void *v, void *out, int32_t B,
+                      int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double rope_base, double alpha,
+                      int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                      size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+    atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < decode_ws_bytes(B, Hq, Hkv, S, d))
+        return ATF_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned long long *counter = (unsigned long long *)workspace;
+    if (dtype == ATF_F32) {
+        AttnArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.q = q;
+        a.krot = k;
+        a.vt = v;
+        a.out = out;
+        a.counter = counter;
+        a.B = B;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.group = Hq / Hkv;
+        a.Sq = 1;
+        a.Sk = (int)S;
+        a.Sk_pad = (int)S;
+        a.q_pos0 = pos0 + S;
+        a.k_pos0 = pos0;
+        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+        window_table_i32(d, rope_base, alpha, a.W);
+        theta_table(d, rope_base, a.theta);
+        if (launch_fill_zero_u64(counter, s) != hipSuccess) return ATF_ERR_HIP;
+        if (launch_attend_f32(a, d, s) != hipSuccess) return ATF_ERR_HIP;
+        return read_counter(counter, skipped_out, s);
+    }
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.counter = counter;
+    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.S = (int)S;
+    a.pos0 = pos0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    DecodePlan plan;
+    plan_decode(B, Hq, Hkv, S, d, a.W, plan);
+    a.nsplit = plan.nsplit;
+    a.n_slabs = plan.n_slabs;
+    std::memcpy(a.split_start, plan.starts, sizeof(int) * (size_t)(plan.nsplit + 1));
+    if (launch_decode_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(counter, skipped_out, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal interface between the host planner (atf_api.cpp) and the HIP
+// kernels (atf_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace atf {
+
+constexpr int kMaxPairs = 64;     // d <= 128
+constexpr int kKeyTile = 64;      // keys per prefill tile / decode chunk
+constexpr int kQueryTile = 128;   // queries per prefill workgroup (bf16)
+constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
+constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
+constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves
+constexpr int kWindowInf = 0x7fffffff;
+
+// Padded key count: every tile is full, padding rows hold zeros.
+inline int64_t padded_keys(int64_t S) { return (S + kKeyTile - 1) / kKeyTile * kKeyTile; }
+
+// Arguments of the key/value preparation pass.
+struct PrepArgs {
+    const void *k;
+    const void *v;
+    void *krot;                       // rotated keys [B][Hkv][S_pad][d]
+    void *vt;                         // bf16 only: transposed value tiles
+    unsigned long long *counter;      // zeroed here
+    int B, Hkv, S, S_pad;
+    long long pos0;
+    double theta[kMaxPairs];
+};
+
+// Arguments of the attention kernels (prefill; the fp32 kernel also decodes).
+struct AttnArgs {
+    const void *q;
+    const void *krot;                 // from the preparation pass
+    const void *vt;                   // bf16: transposed value tiles; fp32: v itself
+    void *out;
+    unsigned long long *counter;      // dropped (query, key, pair) terms
+    int B, Hq, Hkv, group;
+    int Sq, Sk, Sk_pad;               // query rows, keys, padded keys
+    long long q_pos0, k_pos0;         // position of query 0 and key 0
+    int n_qtiles, n_groups;           // work decomposition
+    float scale_log2;                 // log2(e) / sqrt(d)
+    int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)
+    double theta[kMaxPairs];
+};
+
+// Arguments of the split-KV decode kernel and its combine step.
+struct DecodeArgs {
+    const void *q;
+    const void *k;
+    const void *v;
+    float *part;                      // [B*Hq][nsplit][d + 2]  (o..., m, l)
+    void *out;
+    unsigned long long *counter;
+    int B, Hq, Hkv, group, S, nsplit, n_slabs;
+    long long pos0;
+    float scale_log2;
+    int W[kMaxPairs];
+    double theta[kMaxPairs];
+    int split_start[kMaxSplits + 1];  // key index where each split begins (multiple of 64)
+};
+
+hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s);
+hipError_t launch_prep_f32(const PrepArgs &a, int d, hipStream_t s);
+hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s);
+hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s);
+hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s);
+
+}  // namespace atf

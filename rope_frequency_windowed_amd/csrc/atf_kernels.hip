@@ -1,0 +1,837 @@
+// HIP kernels for windowed-RoPE attention on gfx950 (CDNA4).
+//
+// Method (source page "ATFlash: RoPE-Frequenzen kuerzen Attention-Arbeit um
+// bis zu 57 Prozent", sudo-ai.de, section "Was ATFlash anders macht"): rotary
+// pair p keeps its share q'_p k'_p + q'_{p+P} k'_{p+P} of score(i,j) only while
+// the distance i - j is at most W_p, a window proportional to the pair's
+// wavelength; the slowest pair is never cut.  Section "Die Zahlen - und ihre
+// Grenze": the online-softmax recurrence stays as it is.
+//
+// Windows are non-decreasing in p, so at distance D the kept pairs are the
+// suffix [p*(D), P) with p*(D) = #{p : W_p < D}.  Everything below is built on
+// that fact: in the pair-interleaved key layout the kept dims of a tile are
+// one contiguous K-range of the MFMA contraction.
+
+#include "atf_internal.h"
+
+#include <math.h>
+
+namespace atf {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// native vector types (HIP's u32x4/u32x2 are structs and defeat register promotion)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr double kTwoPiHi = 6.283185307179586;       // double nearest to 2*pi
+constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
+constexpr double kInvTwoPi = 0.15915494309189535;
+
+// cos and sin of pos * theta.  The angle is formed and reduced to [-pi, pi]
+// in fp64 (a two-constant 2*pi), so positions up to 2^31 keep ~1e-7 rad
+// accuracy; only the final sincos runs in fp32.
+__device__ inline void rope_cos_sin(long long pos, double theta, float &c, float &s) {
+    const double a = (double)pos * theta;
+    const double k = rint(a * kInvTwoPi);
+    double r = fma(-k, kTwoPiHi, a);
+    r = fma(-k, kTwoPiLo, r);
+    sincosf((float)r, &s, &c);
+}
+
+__device__ inline float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats to a packed bf16 pair, round to nearest even.
+__device__ inline unsigned pack_bf(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ inline float dot2_bf(unsigned a, unsigned b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// LDS swizzles.  A 64-lane ds_read_b128 is served 8 or 16 lanes per pass;
+// these make the 8 and the 16 rows read in one pass land in distinct bank
+// groups for 128-byte rows (swz8) and 256-byte rows (swz16).
+__device__ inline int swz8(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+__device__ inline int swz16(int row) { return row & 15; }
+template <int CH>
+__device__ inline int kswz(int row) { return (CH == 16) ? swz16(row) : swz8(row); }
+
+// ============================================================================
+// Preparation pass (bf16): rotate every key once, store it pair-interleaved
+// (dims (p, p+P) side by side as one 32-bit word), and store the values
+// transposed per 64-key tile, keys permuted inside each group of 16 so that
+// the attention kernel's MFMA operand for P.V is one 16-byte LDS read.
+// grid (S_pad/64, B*Hkv), block 256.
+// ============================================================================
+
+// Key held at position `pos` (0..15) of a 16-key group of a value tile.
+__device__ inline int vt_key_of_pos(int pos) {
+    const int h = pos >> 3, e = pos & 7;
+    return ((e >> 2) << 3) + (h << 2) + (e & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
+    constexpr int P = D / 2;
+    constexpr int PPT = P / 4;  // pairs per thread (16 or 8)
+    const int tile = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    const unsigned short *k = (const unsigned short *)a.k + (long long)bh * a.S * D;
+    const unsigned short *v = (const unsigned short *)a.v + (long long)bh * a.S * D;
+    unsigned *kr = (unsigned *)a.krot + (long long)bh * a.S_pad * P;
+    unsigned short *vt = (unsigned short *)a.vt + ((long long)bh * (a.S_pad / kKeyTile) + tile) * (D * kKeyTile);
+
+    if (tile == 0 && bh == 0 && t == 0) *a.counter = 0ull;
+
+    {  // keys
+        const int row = t >> 2, p0 = (t & 3) * PPT;
+        const int j = tile * kKeyTile + row;
+        union { u32x4 v[PPT / 4]; unsigned w[PPT]; } res;
+        if (j < a.S) {
+            union { u32x4 v[PPT / 8]; unsigned short s[PPT]; } lo, hi;
+            const unsigned short *src = k + (long long)j * D;
+#pragma unroll
+            for (int u = 0; u < PPT / 8; ++u) {
+                lo.v[u] = ((const u32x4 *)(src + p0))[u];
+                hi.v[u] = ((const u32x4 *)(src + P + p0))[u];
+            }
+            const long long pos = a.pos0 + j;
+#pragma unroll
+            for (int u = 0; u < PPT; ++u) {
+                float c, s;
+                rope_cos_sin(pos, a.theta[p0 + u], c, s);
+                const float x = __uint_as_float((unsigned)lo.s[u] << 16);
+                const float y = __uint_as_float((unsigned)hi.s[u] << 16);
+                res.w[u] = pack_bf(x * c - y * s, y * c + x * s);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < PPT; ++u) res.w[u] = 0u;
+        }
+        u32x4 *dst = (u32x4 *)(kr + (long long)j * P + p0);
+#pragma unroll
+        for (int u = 0; u < PPT / 4; ++u) dst[u] = res.v[u];
+    }
+
+    {  // values: tile [64][D] -> LDS -> [D][64] with the in-group key permutation
+        constexpr int LD = D + 8;  // padded LDS row (ushort)
+        __shared__ unsigned short vs[kKeyTile * LD];
+        constexpr int CHR = D / 8;  // 16-byte chunks per row
+#pragma unroll
+        for (int n = 0; n < (kKeyTile * CHR) / 256; ++n) {
+            const int g = t + 256 * n;
+            const int row = g / CHR, ch = g % CHR;
+            const int j = tile * kKeyTile + row;
+            u32x4 val = (u32x4){0u, 0u, 0u, 0u};
+            if (j < a.S) val = *(const u32x4 *)(v + (long long)j * D + ch * 8);
+            *(u32x4 *)(vs + row * LD + ch * 8) = val;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < (D * 8) / 256; ++n) {
+            const int g = t + 256 * n;
+            const int dim = g >> 3, pc = g & 7;
+            union { u32x4 v; unsigned short s[8]; } o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int pos = pc * 8 + e;
+                const int key = (pos & ~15) + vt_key_of_pos(pos & 15);
+                o.s[e] = vs[key * LD + dim];
+            }
+            *(u32x4 *)(vt + dim * kKeyTile + pc * 8) = o.v;
+        }
+    }
+}
+
+// ============================================================================
+// Prefill attention, bf16 in / fp32 accumulate, MFMA 32x32x16.
+//
+// Workgroup = 4 waves = 128 queries of one (b, h); wave w owns 32 queries.
+// Per 64-key tile (double-buffered in LDS) each wave computes two 32x32 score
+// blocks S^T = K' Q'^T (keys on MFMA rows, queries on columns, so one lane
+// holds 16 keys of one query and the softmax row statistics stay in-lane),
+// then O^T += V^T P^T.
+//
+// Windows per 32x32 block: distances span [dmin, dmax]; pairs below
+// p_lo = p*(dmin) are dropped everywhere in the block, pairs from
+// p_full = p*(dmax) on are kept everywhere.  The MFMA K-loop runs only over
+// the 16-dim steps holding pairs >= p_full (pairs below p_full inside the
+// first step are zeroed in the key operand, exact because the block is
+// uniform there).  Each boundary pair p in [p_lo, p_full) gets its own MFMA
+// with a key operand holding only pair p, and is added element by element
+// where distance <= W_p.  Dropped terms are counted exactly.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
+    constexpr int P = D / 2;
+    constexpr int NSTEP = D / 16;   // MFMA K-steps of 16 dims (8 pairs)
+    constexpr int CH = D / 8;       // 16-byte chunks per rotated-key row
+    constexpr int NDB = D / 32;     // 32-dim blocks of the output
+    constexpr int NLD = CH / 4;     // 16-byte global loads per thread per tile (each of K', V^T)
+    __shared__ u32x4 lds_k[2][kKeyTile * CH];
+    __shared__ u32x4 lds_v[2][D * 8];
+
+    // ---- work item: longest query tiles first; the group heads sharing one kv
+    // head run on one XCD (workgroup ids are dealt to the 8 XCDs round robin).
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int gi = (slot / a.group) * 8 + xcd;
+    if (gi >= a.n_groups) return;
+    const int g = slot % a.group;
+    const int per_qt = a.B * a.Hkv;
+    const int qt = a.n_qtiles - 1 - gi / per_qt;
+    const int rem = gi % per_qt;
+    const int b = rem / a.Hkv, hk = rem % a.Hkv;
+    const int h = hk * a.group + g;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int qi = lane & 31, half = lane >> 5;
+    const int i0 = qt * kQueryTile + wave * 32;
+    const int my_q = i0 + qi;
+    const bool q_valid = my_q < a.Sq;
+    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
+
+    // ---- this lane's rotated query, in B-operand order: step s holds pairs
+    // 8s + 4*half + (0..3), each as (x'_p, x'_{p+P}).
+    bf16x8_t qf[NSTEP];
+    {
+        const unsigned short *qrow =
+            (const unsigned short *)a.q + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+        const long long pos = a.q_pos0 + my_q;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+            if (q_valid) {
+                const int p0 = 8 * s + 4 * half;
+                const u32x2 lo = *(const u32x2 *)(qrow + p0);
+                const u32x2 hi = *(const u32x2 *)(qrow + P + p0);
+                unsigned r[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
+                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
+                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
+                    float c, sn;
+                    rope_cos_sin(pos, a.theta[p0 + u], c, sn);
+                    r[u] = pack_bf(x * c - y * sn, y * c + x * sn);
+                }
+                w = (u32x4){r[0], r[1], r[2], r[3]};
+            }
+            qf[s] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+
+    const u32x4 *kg = (const u32x4 *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * CH;
+    const u32x4 *vg = (const u32x4 *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D / 8);
+    const int last_key = min(a.Sk - 1, qt * kQueryTile + kQueryTile - 1);
+    const int n_kt = last_key / kKeyTile + 1;
+
+    u32x4 kbuf[NLD], vbuf[NLD];
+    // global -> registers (next tile) and registers -> swizzled LDS
+#define ATF_GLOAD(kt_)                                                   \
+    {                                                                    \
+        const u32x4 *ks_ = kg + (long long)(kt_) * kKeyTile * CH;        \
+        const u32x4 *vs_ = vg + (long long)(kt_) * D * 8;                \
+        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                \
+            kbuf[n] = ks_[tid + 256 * n];                                \
+            vbuf[n] = vs_[tid + 256 * n];                                \
+        }                                                                \
+    }
+#define ATF_LSTORE(buf_)                                                 \
+    {                                                                    \
+        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                \
+            const int idx = tid + 256 * n;                               \
+            const int row = idx / CH, c = idx % CH;                      \
+            lds_k[buf_][row * CH + (c ^ kswz<CH>(row))] = kbuf[n];       \
+            const int dr = idx >> 3, vc = idx & 7;                       \
+            lds_v[buf_][dr * 8 + (vc ^ swz8(dr))] = vbuf[n];             \
+        }                                                                \
+    }
+
+    f32x16_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    // Running reference max (log2 units) and sum.  The reference is moved only
+    // when a block's max exceeds it by more than kRescale, so probabilities stay
+    // below 2^kRescale and the O rescale is rare; the result is unchanged.
+    constexpr float kRescale = 8.f;
+    constexpr unsigned kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
+    float m_run = -INFINITY, l_run = 0.f;
+    unsigned long long skipped = 0;
+    const f32x16_t zero16 = {};
+    // this lane's key offsets inside a 32-key block: 8*(r/4) + 4*half + r%4
+    const int koff0 = 4 * half;
+
+    ATF_GLOAD(0);
+    ATF_LSTORE(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < n_kt) ATF_GLOAD(kt + 1);
+        const int j0 = kt * kKeyTile;
+
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int jb = j0 + 32 * kb;
+            if (jb > i0 + 31) continue;  // every key after every query of this wave
+            const int dmax = i0 + 31 - jb;
+            const int dmin = max(0, i0 - (jb + 31));
+            const int p_lo = __builtin_popcountll(__ballot(w_lane < dmin));
+            const int p_full = __builtin_popcountll(__ballot(w_lane < dmax));
+            const int s_first = p_full >> 3;
+            const int krow = 32 * kb + qi;
+            const u32x4 *krow_lds = &lds_k[buf][krow * CH];
+            const int ksw = kswz<CH>(krow);
+            const bool diag = jb + 31 > i0;  // some key may follow some query
+
+            // dropped terms of pairs below p_lo: every causal element of the block
+            if (q_valid && p_lo > 0) {
+                int ncausal = 16;
+                if (diag) {
+                    ncausal = 0;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        ncausal += (jb + 8 * (r >> 2) + koff0 + (r & 3) <= my_q) ? 1 : 0;
+                }
+                skipped += (unsigned long long)p_lo * (unsigned)ncausal;
+            }
+
+            f32x16_t sacc = zero16;
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) {
+                if (s >= s_first) {
+                    u32x4 kw = krow_lds[(2 * s + half) ^ ksw];
+                    if (s == s_first) {
+                        const int pb = 8 * s + 4 * half;
+                        kw.x = (pb + 0 < p_full) ? 0u : kw.x;
+                        kw.y = (pb + 1 < p_full) ? 0u : kw.y;
+                        kw.z = (pb + 2 < p_full) ? 0u : kw.z;
+                        kw.w = (pb + 3 < p_full) ? 0u : kw.w;
+                    }
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, kw), qf[s], sacc, 0, 0, 0);
+                }
+            }
+
+            // boundary pairs: one rank-2 MFMA each (key operand holds only pair
+            // p), added where the element's distance is inside W_p
+            if (p_lo < p_full) {
+#pragma unroll
+                for (int s = 0; s < NSTEP; ++s) {
+                    const int pa = max(p_lo, 8 * s), pe = min(p_full, 8 * s + 8);
+                    if (pa < pe) {
+                        const u32x4 kraw = krow_lds[(2 * s + half) ^ ksw];
+                        const int pb = 8 * s + 4 * half;
+                        for (int p = pa; p < pe; ++p) {
+                            u32x4 kw;
+                            kw.x = (pb + 0 == p) ? kraw.x : 0u;
+                            kw.y = (pb + 1 == p) ? kraw.y : 0u;
+                            kw.z = (pb + 2 == p) ? kraw.z : 0u;
+                            kw.w = (pb + 3 == p) ? kraw.w : 0u;
+                            const f32x16_t tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);
+                            const int Wp = __builtin_amdgcn_readlane(w_lane, p);
+                            int ndrop = 0;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int delta = my_q - (jb + 8 * (r >> 2) + koff0 + (r & 3));
+                                const bool keep = delta <= Wp;
+                                sacc[r] += keep ? tp[r] : 0.f;
+                                ndrop += (!keep && delta >= 0) ? 1 : 0;
+                            }
+                            if (q_valid) skipped += (unsigned)ndrop;
+                        }
+                    }
+                }
+            }
+
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[r] = -INFINITY;
+            }
+
+            // ---- online softmax for this block; lane and lane^32 share a query
+            float bm = sacc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
+            bm = fmaxf(bm, __shfl_xor(bm, 32)) * a.scale_log2;
+            const bool move = bm > m_run + kRescale;
+            if (__ballot(move)) {
+                const float m_new = move ? bm : m_run;
+                const float corr = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= corr;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                unsigned pw[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float p0 = fast_exp2(fmaf(sacc[8 * t + 2 * u], a.scale_log2, -m_run));
+                    const float p1 = fast_exp2(fmaf(sacc[8 * t + 2 * u + 1], a.scale_log2, -m_run));
+                    pw[u] = pack_bf(p0, p1);
+                    l_run = dot2_bf(pw[u], kOnesBf16x2, l_run);
+                }
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+                const int vch = 2 * (2 * kb + t) + half;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int vrow = 32 * db + qi;
+                    const u32x4 vw = lds_v[buf][vrow * 8 + (vch ^ swz8(vrow))];
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8_t, vw), pop, o[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (kt + 1 < n_kt) ATF_LSTORE(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3)
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.f / l_tot;
+    if (q_valid) {
+        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                u32x2 w;
+                w.x = pack_bf(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
+                w.y = pack_bf(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
+                *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
+            }
+    }
+    skipped = wave_sum_u64(skipped);
+    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+#undef ATF_GLOAD
+#undef ATF_LSTORE
+}
+
+// ============================================================================
+// fp32 attention (prefill and decode): plain VALU, one query per lane, keys
+// rotated on the fly per 32-key LDS tile, exact per-element window test.
+// Serves the fp32 dtype (parity workloads), not the bf16 hot path.
+// grid (ceil(Sq/64), B*Hq), block 64.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
+    constexpr int P = D / 2;
+    constexpr int TK = 32;
+    __shared__ float2 ks[TK][P];
+    __shared__ float vs[TK][D];
+    const int bh = blockIdx.y;
+    const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
+    const int lane = threadIdx.x;
+    const int qblk0 = blockIdx.x * 64;
+    const int i = qblk0 + lane;
+    const bool valid = i < a.Sq;
+    const long long qpos = a.q_pos0 + i;
+
+    float qx[P], qy[P];
+    {
+        const float *qrow = (const float *)a.q + ((long long)bh * a.Sq + (valid ? i : 0)) * D;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            float c, s;
+            rope_cos_sin(qpos, a.theta[p], c, s);
+            const float x = valid ? qrow[p] : 0.f, y = valid ? qrow[p + P] : 0.f;
+            qx[p] = x * c - y * s;
+            qy[p] = y * c + x * s;
+        }
+    }
+    const float *kh = (const float *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk * D;  // raw keys
+    const float *vh = (const float *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk * D;
+    // last key any query of this block may see
+    const long long qpos_last = a.q_pos0 + min(a.Sq, qblk0 + 64) - 1;
+    const long long kend_ll = min((long long)a.Sk, qpos_last - a.k_pos0 + 1);
+    const int kend = (int)max(0ll, kend_ll);
+
+    float o[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) o[c] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    unsigned long long skipped = 0;
+
+    for (int j0 = 0; j0 < kend; j0 += TK) {
+        __syncthreads();
+        for (int e = lane; e < TK * P; e += 64) {
+            const int jj = e / P, p = e % P, j = j0 + jj;
+            float2 r = make_float2(0.f, 0.f);
+            if (j < kend) {
+                float c, s;
+                rope_cos_sin(a.k_pos0 + j, a.theta[p], c, s);
+                const float x = kh[(long long)j * D + p], y = kh[(long long)j * D + p + P];
+                r = make_float2(x * c - y * s, y * c + x * s);
+            }
+            ks[jj][p] = r;
+        }
+        for (int e = lane; e < TK * D; e += 64) {
+            const int jj = e / D, c = e % D, j = j0 + jj;
+            vs[jj][c] = (j < kend) ? vh[(long long)j * D + c] : 0.f;
+        }
+        __syncthreads();
+        const int nk = min(TK, kend - j0);
+        for (int jj = 0; jj < nk; ++jj) {
+            const long long delta = qpos - (a.k_pos0 + j0 + jj);
+            if (!valid || delta < 0) continue;
+            float s = 0.f;
+            int ndrop = 0;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const float term = qx[p] * ks[jj][p].x + qy[p] * ks[jj][p].y;
+                const bool keep = delta <= (long long)a.W[p];
+                s += keep ? term : 0.f;
+                ndrop += keep ? 0 : 1;
+            }
+            skipped += (unsigned)ndrop;
+            const float x = s * a.scale_log2;
+            const float m_new = fmaxf(m, x);
+            const float corr = exp2f(m - m_new);
+            const float pe = exp2f(x - m_new);
+            l = l * corr + pe;
+#pragma unroll
+            for (int c = 0; c < D; ++c) o[c] = o[c] * corr + pe * vs[jj][c];
+            m = m_new;
+        }
+    }
+    if (valid) {
+        float *orow = (float *)a.out + ((long long)bh * a.Sq + i) * D;
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int c = 0; c < D; ++c) orow[c] = o[c] * inv;
+    }
+    skipped = wave_sum_u64(skipped);
+    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+}
+
+// ============================================================================
+// Split-KV decode, bf16.  One workgroup = (split, b, kv head, slab of <= 8
+// query heads); its 4 waves take 64-key chunks of the split in turn.
+//
+// Scores: lane = key.  A key at distance D keeps pairs [p*(D), P); the lane
+// loads only the 16-byte pieces of its key row holding kept pairs (far keys
+// read few bytes), rotates them with cos/sin from a two-level table (per-chunk
+// coarse angle x per-lane fine angle, both built from fp64-reduced angles),
+// and takes dot products with the group's rotated queries (bf16 dot2).
+// Softmax: per head, wave-wide max/sum, online across chunks.
+// P.V: lane = pair of dims; probabilities of key pairs come from LDS.
+// Each workgroup writes (o, m, l) per head; a combine kernel merges splits.
+// grid (nsplit, B*Hkv*n_slabs), block 256.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+    constexpr int P = D / 2;
+    constexpr int NC8 = P / 8;           // 8-pair pieces per half row
+    constexpr int NDP = D / 2;           // dim pairs
+    constexpr int KPS = 64 / NDP;        // key-pair stride per lane (1 for d=128, 2 for d=64)
+    constexpr int H = kDecodeHeads;
+    __shared__ float2 fine[P][64];       // cos/sin(u * theta_p), u = 0..63
+    __shared__ unsigned qp[P][H];        // rotated query pairs per head (bf16x2)
+    __shared__ float2 coarse[4][P];      // per wave: cos/sin((pos0 + j0) * theta_p)
+    __shared__ unsigned pbuf[4][32][H];  // per wave: key-pair probabilities per head
+    __shared__ int Wsh[64];
+    __shared__ float wm[4][H], wl[4][H];
+
+    const int split = blockIdx.x;
+    const int slab = blockIdx.y % a.n_slabs;
+    const int bk = blockIdx.y / a.n_slabs;
+    const int b = bk / a.Hkv, hk = bk % a.Hkv;
+    const int h0 = hk * a.group + slab * H;
+    const int nh = min(H, a.group - slab * H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const long long qpos = a.pos0 + a.S;
+
+    for (int e = tid; e < P * 64; e += 256) {
+        const int p = e >> 6, u = e & 63;
+        float c, s;
+        rope_cos_sin(u, a.theta[p], c, s);
+        fine[p][u] = make_float2(c, s);
+    }
+    for (int e = tid; e < H * P; e += 256) {
+        const int hh = e / P, p = e % P;
+        unsigned w = 0u;
+        if (hh < nh) {
+            const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + hh) * D;
+            const float x = __uint_as_float((unsigned)qrow[p] << 16);
+            const float y = __uint_as_float((unsigned)qrow[p + P] << 16);
+            float c, s;
+            rope_cos_sin(qpos, a.theta[p], c, s);
+            w = pack_bf(x * c - y * s, y * c + x * s);
+        }
+        qp[p][hh] = w;
+    }
+    if (tid < 64) Wsh[tid] = (tid < P) ? a.W[tid] : kWindowInf;
+    __syncthreads();
+
+    const int ks = a.split_start[split];
+    const int ke = min(a.split_start[split + 1], a.S);
+    const unsigned short *kbase = (const unsigned short *)a.k + (long long)bk * a.S * D;
+    const unsigned short *vbase = (const unsigned short *)a.v + (long long)bk * a.S * D;
+
+    float m_h[H], l_h[H], o0[H], o1[H];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) {
+        m_h[hh] = -INFINITY;
+        l_h[hh] = 0.f;
+        o0[hh] = 0.f;
+        o1[hh] = 0.f;
+    }
+    unsigned long long skipped = 0;
+
+    // p*(delta) = #{p < P-1 : W_p < delta}, by binary lifting over the sorted table
+    auto pstar = [&](int delta) {
+        int c = 0;
+#pragma unroll
+        for (int st = 32; st > 0; st >>= 1)
+            if (c + st <= P - 1 && Wsh[c + st - 1] < delta) c += st;
+        return c;
+    };
+
+    for (int j0 = ks + wave * 64; j0 < ke; j0 += 256) {
+        if (lane < P) {
+            float c, s;
+            rope_cos_sin(a.pos0 + j0, a.theta[lane], c, s);
+            coarse[wave][lane] = make_float2(c, s);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        const int j = j0 + lane;
+        const bool valid = j < ke;
+        const int ps = valid ? pstar(a.S - j) : P;
+        if (valid) skipped += (unsigned long long)ps * (unsigned)nh;
+        const int pmin = pstar(a.S - min(j0 + 63, ke - 1));  // fewest dropped pairs in the chunk
+
+        float sc[H];
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) sc[hh] = 0.f;
+        const unsigned short *krow = kbase + (long long)j * D;
+        for (int c8 = pmin >> 3; c8 < NC8; ++c8) {
+            u32x4 lo = (u32x4){0u, 0u, 0u, 0u}, hi = lo;
+            if (8 * c8 + 8 > ps) {
+                lo = *(const u32x4 *)(krow + 8 * c8);
+                hi = *(const u32x4 *)(krow + P + 8 * c8);
+            }
+            const unsigned lw[4] = {lo.x, lo.y, lo.z, lo.w};
+            const unsigned hw[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int p = 8 * c8 + u;
+                const float x = (u & 1) ? bf_hi(lw[u >> 1]) : bf_lo(lw[u >> 1]);
+                const float y = (u & 1) ? bf_hi(hw[u >> 1]) : bf_lo(hw[u >> 1]);
+                const float2 f = fine[p][lane];
+                const float2 cc = coarse[wave][p];
+                const float cs = f.x * cc.x - f.y * cc.y;
+                const float sn = f.y * cc.x + f.x * cc.y;
+                const unsigned kp = (p < ps) ? 0u : pack_bf(x * cs - y * sn, y * cs + x * sn);
+                const u32x4 qa = *(const u32x4 *)&qp[p][0];
+                const u32x4 qb = *(const u32x4 *)&qp[p][4];
+                sc[0] = dot2_bf(kp, qa.x, sc[0]);
+                sc[1] = dot2_bf(kp, qa.y, sc[1]);
+                sc[2] = dot2_bf(kp, qa.z, sc[2]);
+                sc[3] = dot2_bf(kp, qa.w, sc[3]);
+                sc[4] = dot2_bf(kp, qb.x, sc[4]);
+                sc[5] = dot2_bf(kp, qb.y, sc[5]);
+                sc[6] = dot2_bf(kp, qb.z, sc[6]);
+                sc[7] = dot2_bf(kp, qb.w, sc[7]);
+            }
+        }
+
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+            const float x = valid ? sc[hh] * a.scale_log2 : -INFINITY;
+            const float m_new = fmaxf(m_h[hh], wave_max(x));
+            const float corr = fast_exp2(m_h[hh] - m_new);
+            const float pr = fast_exp2(x - m_new);
+            l_h[hh] = l_h[hh] * corr + wave_sum(pr);
+            o0[hh] *= corr;
+            o1[hh] *= corr;
+            m_h[hh] = m_new;
+            const float pn = __shfl_down(pr, 1);
+            if (!(lane & 1)) pbuf[wave][lane >> 1][hh] = pack_bf(pr, pn);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        const int d2 = lane % NDP;
+        for (int kp = lane / NDP; kp < 32; kp += KPS) {
+            const int ja = j0 + 2 * kp;
+            unsigned w0 = 0u, w1 = 0u;
+            if (ja < ke) w0 = *(const unsigned *)(vbase + (long long)ja * D + 2 * d2);
+            if (ja + 1 < ke) w1 = *(const unsigned *)(vbase + (long long)(ja + 1) * D + 2 * d2);
+            const unsigned va = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // (v[ja][2d2], v[ja+1][2d2])
+            const unsigned vb = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (v[ja][2d2+1], v[ja+1][2d2+1])
+            const u32x4 pa = *(const u32x4 *)&pbuf[wave][kp][0];
+            const u32x4 pb = *(const u32x4 *)&pbuf[wave][kp][4];
+            const unsigned pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) {
+                o0[hh] = dot2_bf(pv[hh], va, o0[hh]);
+                o1[hh] = dot2_bf(pv[hh], vb, o1[hh]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // lanes sharing a dim pair (d = 64) hold disjoint key pairs: add them up
+    if (KPS == 2) {
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+            o0[hh] += __shfl_xor(o0[hh], 32);
+            o1[hh] += __shfl_xor(o1[hh], 32);
+        }
+    }
+
+    // ---- merge the 4 waves (reuses the fine table's LDS) and write partials
+    __syncthreads();
+    float *wo = (float *)&fine[0][0];  // [4][H][D]
+    if (lane < NDP) {
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+            wo[(wave * H + hh) * D + 2 * lane] = o0[hh];
+            wo[(wave * H + hh) * D + 2 * lane + 1] = o1[hh];
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+            wm[wave][hh] = m_h[hh];
+            wl[wave][hh] = l_h[hh];
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < nh * (D + 2); e += 256) {
+        const int hh = e / (D + 2), c = e % (D + 2);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][hh]);
+        float val;
+        if (c == D) {
+            val = M;
+        } else {
+            val = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = (wm[w][hh] == -INFINITY) ? 0.f : fast_exp2(wm[w][hh] - M);
+                val += f * ((c < D) ? wo[(w * H + hh) * D + c] : wl[w][hh]);
+            }
+        }
+        a.part[((long long)(b * a.Hq + h0 + hh) * a.nsplit + split) * (D + 2) + c] = val;
+    }
+    skipped = wave_sum_u64(skipped);
+    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+}
+
+// Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// grid B*Hq, block D.
+template <int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+    const int row = blockIdx.x, c = threadIdx.x;
+    const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float ms = pr[s * (D + 2) + D];
+        if (ms == -INFINITY) continue;
+        const float f = fast_exp2(ms - M);
+        num += f * pr[s * (D + 2) + c];
+        den += f * pr[s * (D + 2) + D + 1];
+    }
+    const float r = num / den;
+    ((__bf16 *)a.out)[(long long)row * D + c] = (__bf16)r;
+}
+
+__global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s) {
+    dim3 grid((unsigned)(a.S_pad / kKeyTile), (unsigned)(a.B * a.Hkv));
+    if (d == 128) prep_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    else prep_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
+    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
+    const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
+    if (d == 128) prefill_bf16_kernel<128><<<n_wg, 256, 0, s>>>(a);
+    else prefill_bf16_kernel<64><<<n_wg, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s) {
+    dim3 grid((unsigned)((a.Sq + 63) / 64), (unsigned)(a.B * a.Hq));
+    if (d == 128) attend_f32_kernel<128><<<grid, 64, 0, s>>>(a);
+    else attend_f32_kernel<64><<<grid, 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
+    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
+    if (d == 128) decode_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    else decode_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d == 128) decode_combine_kernel<128><<<a.B * a.Hq, 128, 0, s>>>(a);
+    else decode_combine_kernel<64><<<a.B * a.Hq, 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s) {
+    fill_zero_u64_kernel<<<1, 1, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace atf

@@ -1,0 +1,142 @@
+"""Host-side checks of librfw_atf.so that need no GPU: the library loads and
+exports every symbol include/atf.h declares, its fp64 window table and closed
+form agree with the (independently written) oracle, and every argument error
+is reported before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import rope_frequency_windowed_amd as atf
+from rope_frequency_windowed_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "atf.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(atf.LIB_PATH):
+        from rope_frequency_windowed_amd import build
+        build.build()
+    return atf.library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[a-z_ ]+\*?\s*\b(atf_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_binding_names():
+    assert header_functions() == sorted(bnd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert atf.atf_version().startswith("rfw-atf")
+
+
+@pytest.mark.parametrize("d,base", [(64, 1e4), (128, 1e6), (128, 1e4), (16, 10.0), (2, 50.0)])
+@pytest.mark.parametrize("alpha", [0.1, 0.5, 1.0, 2.0, 3.7, math.inf])
+def test_window_table_matches_oracle(lib, orc, d, base, alpha):
+    np.testing.assert_array_equal(atf.atf_window_table(d, base, alpha), orc.window_table(d, base, alpha))
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 8, 100, 4097, 32768, 131072, 1 << 20])
+@pytest.mark.parametrize("d,base,alpha", [(64, 1e4, 1.0), (128, 1e6, 0.5), (128, 1e6, 1.0),
+                                          (128, 1e6, 2.0), (128, 1e6, math.inf)])
+def test_closed_form_matches_oracle(lib, orc, S, d, base, alpha):
+    for dec in (0, 1):
+        assert atf.atf_skipped_pair_products(S, d, base, alpha, 1, dec) == \
+            orc.skipped_closed_form(S, d, base, alpha, decode=bool(dec))
+
+
+def test_known_counts(lib):
+    assert atf.atf_skipped_pair_products(256, 64, 1e4, 1.0) == 270074
+
+
+def _call_prefill(lib, **kw):
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, base=1e6, alpha=1.0,
+                causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_prefill(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
+                           ctypes.c_void_p(args["out"]), args["B"], args["Hq"], args["Hkv"], args["S"],
+                           args["d"], args["base"], args["alpha"], args["causal"], args["pos0"],
+                           args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"],
+                           args["stream"])
+
+
+def _call_decode(lib, **kw):
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, base=1e6, alpha=1.0,
+                causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_decode(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
+                          ctypes.c_void_p(args["out"]), args["B"], args["Hq"], args["Hkv"], args["S"],
+                          args["d"], args["base"], args["alpha"], args["causal"], args["pos0"],
+                          args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"],
+                          args["stream"])
+
+
+# Every case below fails validation, so nothing reaches the GPU runtime.
+BAD = [
+    (dict(q=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(k=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(out=8), bnd.ATF_ERR_INVALID_ARG),            # misaligned
+    (dict(B=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(Hq=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(Hq=5, Hkv=2), bnd.ATF_ERR_INVALID_ARG),      # Hq % Hkv != 0
+    (dict(S=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=63), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(d=256), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(base=1.0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(base=float("inf")), bnd.ATF_ERR_INVALID_ARG),
+    (dict(alpha=0.0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(alpha=-2.0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG),
+    (dict(causal=0), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(causal=2), bnd.ATF_ERR_INVALID_ARG),
+    (dict(dtype=7), bnd.ATF_ERR_INVALID_ARG),
+    (dict(pos0=-1), bnd.ATF_ERR_INVALID_ARG),
+    (dict(pos0=(1 << 31) - 100), bnd.ATF_ERR_INVALID_ARG),
+    (dict(ws=None), bnd.ATF_ERR_WORKSPACE),
+    (dict(ws_bytes=1), bnd.ATF_ERR_WORKSPACE),         # undersized (valid otherwise)
+    (dict(Hq=128, Hkv=1), bnd.ATF_ERR_UNSUPPORTED),    # group > 64
+]
+
+
+@pytest.mark.parametrize("kw,expect", BAD)
+def test_prefill_rejects(lib, kw, expect):
+    assert _call_prefill(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", BAD)
+def test_decode_rejects(lib, kw, expect):
+    assert _call_decode(lib, **kw) == expect
+
+
+def test_workspace_sizes(lib):
+    assert atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) == 256 + 2 * 4 * 131072 * 128 * 2
+    assert atf.atf_prefill_workspace_bytes(1, 4, 100, 128, atf.ATF_BF16) == 256 + 2 * 4 * 128 * 128 * 2
+    assert atf.atf_prefill_workspace_bytes(1, 1, 256, 64, atf.ATF_F32) == 256
+    assert atf.atf_prefill_workspace_bytes(1, 1, 256, 96, atf.ATF_BF16) == 0
+    ws = atf.atf_decode_workspace_bytes(8, 28, 4, 262144, 128)
+    assert ws == 256 + 8 * 28 * 64 * 130 * 4
+    assert atf.atf_decode_workspace_bytes(1, 1, 1, 10, 128) == 256 + 1 * 1 * 1 * 130 * 4
+    assert atf.atf_decode_workspace_bytes(1, 3, 2, 10, 128) == 0
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.atf_status_string(code).decode().startswith("ATF_")
+
+
+def test_python_binding_needs_gpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        atf.atf_prefill(q, q, q, rope_base=1e4, alpha=1.0)

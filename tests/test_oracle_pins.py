@@ -292,6 +292,17 @@ def test_rows_subset_matches_full(orc):
         np.testing.assert_array_equal(sub[r], full[b, h, i])
 
 
+def test_compact_query_rows_match_full(orc):
+    B, Hq, Hkv, S, d = 1, 4, 1, 90, 32
+    q, k, v = rnd((B, Hq, S, d), 141), rnd((B, Hkv, S, d), 142), rnd((B, Hkv, S, d), 143)
+    rows = np.array([[0, 3, 89], [0, 0, 0], [0, 2, 45]])
+    full, sf = orc.attention(q, k, v, base=1e4, alpha=0.7, rows=rows)
+    qc = np.stack([q[b, h, i] for b, h, i in rows])
+    comp, sc = orc.attention(qc, k, v, base=1e4, alpha=0.7, rows=rows, q_shape=q.shape)
+    np.testing.assert_array_equal(full, comp)
+    assert sf == sc
+
+
 def test_windows_change_the_output(orc):
     """A discrimination check: at a short window the windowed output differs
     clearly from dense attention."""

@@ -1,0 +1,51 @@
+"""Sizes the bf16 parity bound on the CPU: emulates a kernel whose only error
+is bf16 rounding of its operands (rotated q and k, probabilities, values; all
+products and sums exact) and checks that this inherent error sits well inside
+the bounds the GPU parity tests use, for the iid inputs and for the
+structured (fast pairs x1.5) inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dense_ref
+from parity import BF16_ATOL
+from rope_frequency_windowed_amd.inputs import make_qkv
+
+
+def bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+
+
+def emulate_bf16_operands(orc, q, k, v, base, alpha):
+    q, k, v = (t.double().numpy() for t in (q, k, v))
+    S, d = q.shape[2], q.shape[3]
+    P = d // 2
+    W = orc.window_table(d, base, alpha).astype(np.float64)
+    W[orc.window_table(d, base, alpha) == orc.W_INF] = np.inf
+    pos = np.arange(S)
+    qr = bf16(dense_ref.rope_half_split(q, pos, base))
+    kr = np.repeat(bf16(dense_ref.rope_half_split(k, pos, base)), q.shape[1] // k.shape[1], 1)
+    vv = np.repeat(v, q.shape[1] // k.shape[1], 1)
+    delta = pos[:, None] - pos[None, :]
+    s = np.zeros(q.shape[:2] + (S, S))
+    for p in range(P):
+        t = (qr[..., p][..., :, None] * kr[..., p][..., None, :]
+             + qr[..., p + P][..., :, None] * kr[..., p + P][..., None, :])
+        s += np.where(delta <= W[p], t, 0.0)
+    lg = np.where(delta >= 0, s / math.sqrt(d), -np.inf)
+    w = bf16(np.exp(lg - lg.max(-1, keepdims=True)))
+    return (w @ vv) / w.sum(-1, keepdims=True)
+
+
+@pytest.mark.parametrize("hf", [None, 1.5])
+@pytest.mark.parametrize("alpha", [0.5, 1.0])
+def test_bf16_rounding_fits_the_bound(orc, hf, alpha):
+    q, k, v = make_qkv(1, 2, 1, 600, 600, 128, dtype=torch.bfloat16, high_freq_scale=hf)
+    ref, _ = orc.attention(q, k, v, base=1e6, alpha=alpha)
+    em = emulate_bf16_operands(orc, q, k, v, 1e6, alpha)
+    err, scale = np.abs(em - ref).max(), np.abs(ref).max()
+    bound = BF16_ATOL * (max(1.0, scale) if hf else 1.0)
+    assert err <= 0.5 * bound
+    assert err <= 0.5 * 1e-2 * scale
