@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the windowed-RoPE attention hot path on one MI355X.
+
+One step = one causal prefill of S=131072 tokens (B=1, Hq=28, Hkv=4, d=128,
+RoPE base 1e6, alpha=1, bf16 with fp32 accumulation) followed by one decode
+step (B=8 sequences, one query each after a 262144-key cache, same heads),
+inputs iid N(0,1) from fixed seeds, already resident in HBM.
+
+Printed: one JSON line.  `value` is prefill tokens/s; the `roofline` object
+is for the dominant kernel (the prefill attention kernel, MFMA-bound; the
+algorithmic flops count only the pair products the windows keep plus P.V);
+`decode` carries the decode step's algorithmic HBM rate against its roofline;
+`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+
+  python bench.py [--steps K] [--warmup W] [--only prefill|decode] [--no-cpu]
+  python bench.py --copy-probe      (plain copy kernel of known size, for the
+                                     HBM-counter scale factor)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + MFMA util @S=128K; decode HBM GB/s @256K KV (1 GPU)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
+KERNEL_SRC = os.path.join(ROOT, "rope_frequency_windowed_amd", "csrc", "atf_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_counters.txt")
+
+PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
+DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_algorithmic_flops(atf, B, Hq, S, d, base, alpha, **_):
+    """4 flops per kept (query, key, pair) product + 2d per causal (query, key) for P.V."""
+    P = d // 2
+    n_causal = S * (S + 1) // 2
+    skipped = atf.atf_skipped_pair_products(S, d, base, alpha, 1, 0)
+    return B * Hq * (4 * (P * n_causal - skipped) + 2 * d * n_causal)
+
+
+def decode_algorithmic_bytes(atf, B, Hq, Hkv, S, d, base, alpha, **_):
+    """Kept key pairs (4 bytes each) + every value row + q and out, bf16."""
+    W = atf.atf_window_table(d, base, alpha)
+    kept_pairs = sum(min(S, int(w)) for w in W)
+    return B * Hkv * (4 * kept_pairs + 2 * d * S) + 2 * B * Hq * d * 2
+
+
+def source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """Counter-measured HBM bytes per prefill-attention launch, if the summary
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(q, k, v, cfg, seconds_hint=12.0):
+    """Time the fp64 oracle on a bounded, seeded sample of prefill rows."""
+    import numpy as np
+
+    import oracle
+    from rope_frequency_windowed_amd.inputs import sample_rows
+    B, Hq, Hkv, S, d = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["d"]
+    per_head = 640  # ~10-15 s of oracle work on a 16-core host
+    rows = []
+    for h in range(Hq):
+        for i in sample_rows(S, per_head, seed=100 + h):
+            rows.append((0, h, int(i)))
+    rows = np.array(rows, dtype=np.int64)
+    import torch
+    sel = torch.as_tensor(rows, device=q.device)
+    qrows = q[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    kk = k.float().cpu().numpy()
+    vv = v.float().cpu().numpy()
+    oracle.build()
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    oracle.attention(qrows, kk, vv, base=cfg["base"], alpha=cfg["alpha"], rows=rows,
+                     q_shape=(B, Hq, S, d))
+    dt = time.perf_counter() - t0
+    visits = float(np.sum(rows[:, 2] + 1))
+    total_visits = B * Hq * S * (S + 1) / 2.0
+    full_seconds = dt * total_visits / visits
+    return {
+        "value": B * S / full_seconds,
+        "unit": "tok/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("%d query rows (%d per head, seeded, incl. first and last) of the S=%d layer: "
+                   "%.3g key visits in %.2f s incl. rotating the 4 key heads; tok/s extrapolated "
+                   "linearly in key visits to the full layer (%.3g visits)"
+                   % (len(rows), per_head, S, visits, dt, total_visits)),
+    }
+
+
+def copy_probe():
+    """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB), 5 times: the
+    reference for scaling FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    import rope_frequency_windowed_amd as atf
+    from rope_frequency_windowed_amd.inputs import make_qkv
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
+
+    if do_prefill:
+        P = PREFILL
+        q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], P["S"], P["S"], P["d"], dtype=torch.bfloat16, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], P["S"], P["d"], atf.ATF_BF16),
+                         dtype=torch.uint8, device=dev)
+        # one checked call: the kernel's dropped-term count must equal the closed form
+        atf.atf_prefill_prepare_kv(k, v, rope_base=P["base"], pos0=0, ws=ws)
+        got = atf.atf_prefill_attend(q, k, v, out, rope_base=P["base"], alpha=P["alpha"], ws=ws,
+                                     return_skipped=True)
+        want = P["B"] * P["Hq"] * atf.atf_skipped_pair_products(P["S"], P["d"], P["base"], P["alpha"])
+        if got != want:
+            raise SystemExit("prefill dropped-term count %d != closed form %d" % (got, want))
+    if do_decode:
+        D = DECODE
+        dq, dk, dv = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
+        dout = torch.empty_like(dq)
+        dws = torch.empty(atf.atf_decode_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
+                          dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if do_prefill:
+            if ev is not None:
+                ev[0].record(stream)
+            atf.atf_prefill_prepare_kv(k, v, rope_base=P["base"], pos0=0, ws=ws)
+            if ev is not None:
+                ev[1].record(stream)
+            atf.atf_prefill_attend(q, k, v, out, rope_base=P["base"], alpha=P["alpha"], ws=ws)
+            if ev is not None:
+                ev[2].record(stream)
+        if do_decode:
+            if ev is not None:
+                ev[3].record(stream)
+            atf.atf_decode(dq, dk, dv, dout, rope_base=D["base"], alpha=D["alpha"], ws=dws)
+            if ev is not None:
+                ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": 1e3 * wall / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    config = {"workload": "causal windowed-RoPE prefill S=131072 + decode B=8 KV=262144 (Hq=28, Hkv=4, "
+                          "d=128, RoPE base 1e6, alpha=1), iid N(0,1) seeds 1000/1001/1002"}
+    if do_prefill:
+        prep_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+        attend_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+        prefill_ms = prep_ms + attend_ms
+        flops = prefill_algorithmic_flops(atf, **PREFILL)
+        achieved = flops / (attend_ms * 1e-3) / 1e12
+        res["value"] = PREFILL["B"] * PREFILL["S"] / (prefill_ms * 1e-3)
+        res["unit"] = "tok/s"
+        res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                           "traffic": read_traffic(), "kernel": "prefill_bf16_kernel<128>",
+                           "kernel_ms": attend_ms, "algorithmic_flops_per_launch": flops}
+        config["prefill"] = dict(PREFILL, prep_ms=prep_ms, attend_ms=attend_ms)
+        log("prefill: prep %.3f ms, attend %.3f ms, %.1f TFLOP/s algorithmic (%.1f%% of bf16 peak), %.0f tok/s"
+            % (prep_ms, attend_ms, achieved, 100 * achieved / MFMA_BF16_PEAK_TFLOPS, res["value"]))
+    if do_decode:
+        dec_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
+        nbytes = decode_algorithmic_bytes(atf, **DECODE)
+        gbs = nbytes / (dec_ms * 1e-3) / 1e9
+        res["decode"] = {"value": gbs, "unit": "GB/s", "ms": dec_ms, "tok_per_s": DECODE["B"] / (dec_ms * 1e-3),
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+        config["decode"] = dict(DECODE)
+        log("decode: %.3f ms, %.3g algorithmic bytes, %.0f GB/s (%.1f%% of HBM peak)"
+            % (dec_ms, nbytes, gbs, 100 * gbs / HBM_PEAK_GBS))
+        if not do_prefill:
+            res["value"], res["unit"] = gbs, "GB/s"
+    res["config"] = config
+    if do_prefill and not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(q, k, v, PREFILL)
+        log("cpu baseline:", res["cpu_baseline"])
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
