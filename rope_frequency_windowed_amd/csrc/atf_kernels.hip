@@ -173,20 +173,88 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // Prefill attention, bf16 in / fp32 accumulate, MFMA 32x32x16.
 //
 // Workgroup = 4 waves = 128 queries of one (b, h); wave w owns 32 queries.
-// Per 64-key tile (double-buffered in LDS) each wave computes two 32x32 score
-// blocks S^T = K' Q'^T (keys on MFMA rows, queries on columns, so one lane
-// holds 16 keys of one query and the softmax row statistics stay in-lane),
-// then O^T += V^T P^T.
+// Key tiles of 64 keys stream global -> LDS with direct LDS loads
+// (global_load_lds_dwordx4, no staging registers), double-buffered, one
+// barrier per tile.  Per tile each wave computes two 32x32 score blocks
+// S^T = K' Q'^T (keys on MFMA rows, queries on columns: a lane holds 16 keys
+// of one query, its partner lane^32 the other 16, so softmax row statistics
+// need one lane swap), then O^T += V^T P^T.  Both blocks' score MFMAs are
+// issued before the first block's softmax so the VALU work overlaps them.
 //
 // Windows per 32x32 block: distances span [dmin, dmax]; pairs below
 // p_lo = p*(dmin) are dropped everywhere in the block, pairs from
 // p_full = p*(dmax) on are kept everywhere.  The MFMA K-loop runs only over
-// the 16-dim steps holding pairs >= p_full (pairs below p_full inside the
-// first step are zeroed in the key operand, exact because the block is
-// uniform there).  Each boundary pair p in [p_lo, p_full) gets its own MFMA
-// with a key operand holding only pair p, and is added element by element
-// where distance <= W_p.  Dropped terms are counted exactly.
+// the 16-dim steps holding pairs >= p_full; pairs below p_full inside the
+// first step are zeroed in the key operand (exact: the block is uniform
+// there).  The loop is one of NSTEP straight-line variants chosen once per
+// block, so its LDS reads can be hoisted.  Each boundary pair p in
+// [p_lo, p_full) gets its own MFMA with a key operand holding only pair p,
+// added element by element where the distance is within W_p.  Dropped terms
+// are counted exactly.
+//
+// Scores come out in log2 units minus the running reference: q' is
+// pre-scaled by log2(e)/sqrt(d) and the first MFMA of each block starts from
+// C = -m_ref, so a probability is one exp2 of the accumulator.
 // ============================================================================
+
+__device__ inline float partner_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float partner_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane, global -> LDS, no registers: lane l of the wave writes
+// LDS bytes [dst + 16 l, dst + 16 l + 16); dst must be wave-uniform.
+__device__ inline void lds_dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
+}
+
+// One block's main score chain starting at K-step S0 (compile time).
+// kaddr(s) = kbase + ((32 s) ^ ky): the swizzled byte address of this lane's
+// 16 key dims of step s.
+template <int NSTEP, int S0>
+__device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, unsigned ky,
+                                    const bf16x8_t *qf, const f32x16_t &cinit, int zero_below) {
+    u32x4 kw = *(const u32x4 *)(lds + kbase + ((32u * S0) ^ ky));
+    // words (pairs) of the first step below p_full are dropped or boundary
+    kw.x = (0 < zero_below) ? 0u : kw.x;
+    kw.y = (1 < zero_below) ? 0u : kw.y;
+    kw.z = (2 < zero_below) ? 0u : kw.z;
+    kw.w = (3 < zero_below) ? 0u : kw.w;
+    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], cinit, 0, 0, 0);
+#pragma unroll
+    for (int s = S0 + 1; s < NSTEP; ++s) {
+        const u32x4 k2 = *(const u32x4 *)(lds + kbase + ((32u * s) ^ ky));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, k2), qf[s], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <int NSTEP>
+__device__ inline f32x16_t qk_main(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
+                                   const bf16x8_t *qf, const f32x16_t &cinit, int zero_below) {
+    switch (s_first) {
+        case 0: return qk_chain<NSTEP, 0>(lds, kbase, ky, qf, cinit, zero_below);
+        case 1: return qk_chain<NSTEP, 1>(lds, kbase, ky, qf, cinit, zero_below);
+        case 2: return qk_chain<NSTEP, 2>(lds, kbase, ky, qf, cinit, zero_below);
+        case 3: return qk_chain<NSTEP, 3>(lds, kbase, ky, qf, cinit, zero_below);
+        default: break;
+    }
+    if constexpr (NSTEP > 4) {
+        switch (s_first) {
+            case 4: return qk_chain<NSTEP, 4>(lds, kbase, ky, qf, cinit, zero_below);
+            case 5: return qk_chain<NSTEP, 5>(lds, kbase, ky, qf, cinit, zero_below);
+            case 6: return qk_chain<NSTEP, 6>(lds, kbase, ky, qf, cinit, zero_below);
+            default: return qk_chain<NSTEP, (NSTEP > 4 ? 7 : 3)>(lds, kbase, ky, qf, cinit, zero_below);
+        }
+    }
+    return qk_chain<NSTEP, NSTEP - 1>(lds, kbase, ky, qf, cinit, zero_below);
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
@@ -194,9 +262,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     constexpr int NSTEP = D / 16;   // MFMA K-steps of 16 dims (8 pairs)
     constexpr int CH = D / 8;       // 16-byte chunks per rotated-key row
     constexpr int NDB = D / 32;     // 32-dim blocks of the output
-    constexpr int NLD = CH / 4;     // 16-byte global loads per thread per tile (each of K', V^T)
-    __shared__ u32x4 lds_k[2][kKeyTile * CH];
-    __shared__ u32x4 lds_v[2][D * 8];
+    constexpr int NLD = CH / 4;     // 1 KB direct loads per wave per tile (each of K', V^T)
+    constexpr unsigned KT_BYTES = kKeyTile * D * 2;
+    constexpr unsigned TILE_BYTES = 2 * KT_BYTES;  // K' then V^T
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
 
     // ---- work item: longest query tiles first; the group heads sharing one kv
     // head run on one XCD (workgroup ids are dealt to the 8 XCDs round robin).
@@ -218,13 +287,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     const bool q_valid = my_q < a.Sq;
     const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
 
-    // ---- this lane's rotated query, in B-operand order: step s holds pairs
-    // 8s + 4*half + (0..3), each as (x'_p, x'_{p+P}).
+    // ---- this lane's rotated, pre-scaled query in B-operand order: step s
+    // holds pairs 8s + 4*half + (0..3), each as (x'_p, x'_{p+P}) * log2(e)/sqrt(d)
     bf16x8_t qf[NSTEP];
     {
         const unsigned short *qrow =
             (const unsigned short *)a.q + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
         const long long pos = a.q_pos0 + my_q;
+        const float sc = a.scale_log2;
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
@@ -240,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                     const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
                     float c, sn;
                     rope_cos_sin(pos, a.theta[p0 + u], c, sn);
-                    r[u] = pack_bf(x * c - y * sn, y * c + x * sn);
+                    r[u] = pack_bf((x * c - y * sn) * sc, (y * c + x * sn) * sc);
                 }
                 w = (u32x4){r[0], r[1], r[2], r[3]};
             }
@@ -248,31 +318,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         }
     }
 
-    const u32x4 *kg = (const u32x4 *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * CH;
-    const u32x4 *vg = (const u32x4 *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D / 8);
+    const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
+    const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const int last_key = min(a.Sk - 1, qt * kQueryTile + kQueryTile - 1);
     const int n_kt = last_key / kKeyTile + 1;
 
-    u32x4 kbuf[NLD], vbuf[NLD];
-    // global -> registers (next tile) and registers -> swizzled LDS
-#define ATF_GLOAD(kt_)                                                   \
-    {                                                                    \
-        const u32x4 *ks_ = kg + (long long)(kt_) * kKeyTile * CH;        \
-        const u32x4 *vs_ = vg + (long long)(kt_) * D * 8;                \
-        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                \
-            kbuf[n] = ks_[tid + 256 * n];                                \
-            vbuf[n] = vs_[tid + 256 * n];                                \
-        }                                                                \
+    // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
+    // wave's n-th 1 KB piece lands at LDS byte piece*1024 + 16 l (lane-linear),
+    // so the lane fetches the global chunk that the swizzle puts there.  Key
+    // chunks whose pairs no block of this workgroup can use are not fetched
+    // (c_min: first 16-byte chunk any wave reads in this tile).
+    // per-lane byte offsets of this wave's direct-load pieces (loop invariant)
+    unsigned k_goff[NLD], v_goff[NLD];
+    int k_chunk[NLD];
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+        const int kbyte = (wave * NLD + n) * 1024 + lane * 16;
+        const int krow = kbyte / (CH * 16);
+        k_chunk[n] = ((kbyte / 16) % CH) ^ kswz<CH>(krow);
+        k_goff[n] = (unsigned)(krow * (CH * 16) + k_chunk[n] * 16);
+        const int vrow = kbyte / 128;
+        v_goff[n] = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
     }
-#define ATF_LSTORE(buf_)                                                 \
-    {                                                                    \
-        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                \
-            const int idx = tid + 256 * n;                               \
-            const int row = idx / CH, c = idx % CH;                      \
-            lds_k[buf_][row * CH + (c ^ kswz<CH>(row))] = kbuf[n];       \
-            const int dr = idx >> 3, vc = idx & 7;                       \
-            lds_v[buf_][dr * 8 + (vc ^ swz8(dr))] = vbuf[n];             \
-        }                                                                \
+#define ATF_TILE_LOAD(kt_, buf_)                                                           \
+    {                                                                                      \
+        const int j0_ = (kt_) * kKeyTile;                                                  \
+        const int dmin_wg_ = max(0, qt * kQueryTile - (j0_ + kKeyTile - 1));               \
+        const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
+        const unsigned char *ks_ = kg + (long long)j0_ * (D * 2);                          \
+        const unsigned char *vs_ = vg + (long long)j0_ * (D * 2);                          \
+        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave * (NLD * 1024);              \
+        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
+            if (k_chunk[n] >= c_min_)                                                      \
+                lds_dma16(ks_ + k_goff[n], lk_ + n * 1024);                                \
+            lds_dma16(vs_ + v_goff[n], lk_ + KT_BYTES + n * 1024);                         \
+        }                                                                                  \
     }
 
     f32x16_t o[NDB];
@@ -280,38 +360,53 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    // Running reference max (log2 units) and sum.  The reference is moved only
-    // when a block's max exceeds it by more than kRescale, so probabilities stay
-    // below 2^kRescale and the O rescale is rare; the result is unchanged.
+    // Reference max m_ref (log2 units) and running sum.  m_ref moves only when
+    // a block's max exceeds it by more than kRescale (and at the first block),
+    // so probabilities stay below 2^kRescale and the O rescale is rare.
     constexpr float kRescale = 8.f;
     constexpr unsigned kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = 0.f, l_run = 0.f;
     unsigned long long skipped = 0;
     const f32x16_t zero16 = {};
-    // this lane's key offsets inside a 32-key block: 8*(r/4) + 4*half + r%4
     const int koff0 = 4 * half;
+    // per-lane LDS byte offsets (swizzle folded in)
+    const unsigned krow0 = (unsigned)qi;  // key row of block 0; block 1 is +32 rows
+    const unsigned kbase_lane = krow0 * (CH * 16);
+    const unsigned ky = (unsigned)((kswz<CH>(qi) ^ half) << 4);
+    const unsigned vbase_lane = KT_BYTES + (unsigned)qi * 128;
+    const unsigned vz = (unsigned)((swz8(qi) ^ half) << 4);
 
-    ATF_GLOAD(0);
-    ATF_LSTORE(0);
+    ATF_TILE_LOAD(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int kt = 0; kt < n_kt; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < n_kt) ATF_GLOAD(kt + 1);
+        if (kt + 1 < n_kt) ATF_TILE_LOAD(kt + 1, buf ^ 1);
+        const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * kKeyTile;
 
+        // ---- scores of both 32-key blocks: main chain, then that block's
+        // boundary pairs; the second block's MFMAs overlap the first block's softmax
+        f32x16_t sacc[2];
+        bool live[2];
+        float m_issue = m_ref;  // reference both blocks were started from
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jb = j0 + 32 * kb;
-            if (jb > i0 + 31) continue;  // every key after every query of this wave
+            live[kb] = jb <= i0 + 31;
+            sacc[kb] = zero16;
+            if (!live[kb]) continue;
             const int dmax = i0 + 31 - jb;
             const int dmin = max(0, i0 - (jb + 31));
             const int p_lo = __builtin_popcountll(__ballot(w_lane < dmin));
             const int p_full = __builtin_popcountll(__ballot(w_lane < dmax));
             const int s_first = p_full >> 3;
-            const int krow = 32 * kb + qi;
-            const u32x4 *krow_lds = &lds_k[buf][krow * CH];
-            const int ksw = kswz<CH>(krow);
+            const unsigned kbase = kbase_lane + 32u * kb * (CH * 16);
+            f32x16_t cinit;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cinit[r] = -m_issue;
+            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, cinit, p_full - 8 * s_first - koff0);
             const bool diag = jb + 31 > i0;  // some key may follow some query
 
             // dropped terms of pairs below p_lo: every causal element of the block
@@ -326,23 +421,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                 skipped += (unsigned long long)p_lo * (unsigned)ncausal;
             }
 
-            f32x16_t sacc = zero16;
-#pragma unroll
-            for (int s = 0; s < NSTEP; ++s) {
-                if (s >= s_first) {
-                    u32x4 kw = krow_lds[(2 * s + half) ^ ksw];
-                    if (s == s_first) {
-                        const int pb = 8 * s + 4 * half;
-                        kw.x = (pb + 0 < p_full) ? 0u : kw.x;
-                        kw.y = (pb + 1 < p_full) ? 0u : kw.y;
-                        kw.z = (pb + 2 < p_full) ? 0u : kw.z;
-                        kw.w = (pb + 3 < p_full) ? 0u : kw.w;
-                    }
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, kw), qf[s], sacc, 0, 0, 0);
-                }
-            }
-
             // boundary pairs: one rank-2 MFMA each (key operand holds only pair
             // p), added where the element's distance is inside W_p
             if (p_lo < p_full) {
@@ -350,8 +428,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                 for (int s = 0; s < NSTEP; ++s) {
                     const int pa = max(p_lo, 8 * s), pe = min(p_full, 8 * s + 8);
                     if (pa < pe) {
-                        const u32x4 kraw = krow_lds[(2 * s + half) ^ ksw];
-                        const int pb = 8 * s + 4 * half;
+                        const u32x4 kraw = *(const u32x4 *)(lt + kbase + ((32u * s) ^ ky));
+                        const int pb = 8 * s + koff0;
                         for (int p = pa; p < pe; ++p) {
                             u32x4 kw;
                             kw.x = (pb + 0 == p) ? kraw.x : 0u;
@@ -366,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                             for (int r = 0; r < 16; ++r) {
                                 const int delta = my_q - (jb + 8 * (r >> 2) + koff0 + (r & 3));
                                 const bool keep = delta <= Wp;
-                                sacc[r] += keep ? tp[r] : 0.f;
+                                sacc[kb][r] += keep ? tp[r] : 0.f;
                                 ndrop += (!keep && delta >= 0) ? 1 : 0;
                             }
                             if (q_valid) skipped += (unsigned)ndrop;
@@ -374,58 +452,72 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                     }
                 }
             }
+        }
 
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (!live[kb]) continue;
+            const int jb = j0 + 32 * kb;
+            const bool diag = jb + 31 > i0;
+
+            // accumulator = score - m_issue (log2 units); bring it to the current reference
+            if (m_issue != m_ref) {  // a rescale happened after this block was issued
+                const float adj = m_issue - m_ref;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] += adj;
+            }
             if (diag) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[r] = -INFINITY;
+                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[kb][r] = -INFINITY;
             }
 
-            // ---- online softmax for this block; lane and lane^32 share a query
-            float bm = sacc[0];
+            // ---- online softmax for this block (lane and lane^32 share a query)
+            float bm = sacc[kb][0];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[r]);
-            bm = fmaxf(bm, __shfl_xor(bm, 32)) * a.scale_log2;
-            const bool move = bm > m_run + kRescale;
+            for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);
+            bm = partner_max(bm);
+            const bool move = (kt == 0 && kb == 0) || bm > kRescale;
             if (__ballot(move)) {
-                const float m_new = move ? bm : m_run;
-                const float corr = fast_exp2(m_run - m_new);
-                m_run = m_new;
+                const float shift = move ? bm : 0.f;   // new reference = m_ref + shift
+                const float corr = fast_exp2(-shift);
+                m_ref += shift;
                 l_run *= corr;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 unsigned pw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float p0 = fast_exp2(fmaf(sacc[8 * t + 2 * u], a.scale_log2, -m_run));
-                    const float p1 = fast_exp2(fmaf(sacc[8 * t + 2 * u + 1], a.scale_log2, -m_run));
+                    const float p0 = fast_exp2(sacc[kb][8 * t + 2 * u]);
+                    const float p1 = fast_exp2(sacc[kb][8 * t + 2 * u + 1]);
                     pw[u] = pack_bf(p0, p1);
                     l_run = dot2_bf(pw[u], kOnesBf16x2, l_run);
                 }
                 const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
-                const int vch = 2 * (2 * kb + t) + half;
+                const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int vrow = 32 * db + qi;
-                    const u32x4 vw = lds_v[buf][vrow * 8 + (vch ^ swz8(vrow))];
+                    const u32x4 vw = *(const u32x4 *)(lt + vaddr + db * (32 * 128));
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8_t, vw), pop, o[db], 0, 0, 0);
                 }
             }
         }
 
-        if (kt + 1 < n_kt) ATF_LSTORE(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile
         __syncthreads();
     }
+#undef ATF_TILE_LOAD
 
     // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3)
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const float inv = 1.f / l_tot;
+    const float inv = 1.f / partner_sum(l_run);
     if (q_valid) {
         unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
 #pragma unroll
@@ -440,8 +532,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     }
     skipped = wave_sum_u64(skipped);
     if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
-#undef ATF_GLOAD
-#undef ATF_LSTORE
 }
 
 // ============================================================================
