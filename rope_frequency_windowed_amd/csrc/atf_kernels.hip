@@ -192,9 +192,8 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // added element by element where the distance is within W_p.  Dropped terms
 // are counted exactly.
 //
-// Scores come out in log2 units minus the running reference: q' is
-// pre-scaled by log2(e)/sqrt(d) and the first MFMA of each block starts from
-// C = -m_ref, so a probability is one exp2 of the accumulator.
+// Scores come out in log2 units: q' is pre-scaled by log2(e)/sqrt(d), so a
+// probability is 2^(score - m_ref) for the running reference m_ref.
 // ============================================================================
 
 __device__ inline float partner_max(float x) {
@@ -219,14 +218,15 @@ __device__ inline void lds_dma16(const void *src, void *dst) {
 // 16 key dims of step s.
 template <int NSTEP, int S0>
 __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, unsigned ky,
-                                    const bf16x8_t *qf, const f32x16_t &cinit, int zero_below) {
+                                    const bf16x8_t *qf, int zero_below) {
     u32x4 kw = *(const u32x4 *)(lds + kbase + ((32u * S0) ^ ky));
     // words (pairs) of the first step below p_full are dropped or boundary
     kw.x = (0 < zero_below) ? 0u : kw.x;
     kw.y = (1 < zero_below) ? 0u : kw.y;
     kw.z = (2 < zero_below) ? 0u : kw.z;
     kw.w = (3 < zero_below) ? 0u : kw.w;
-    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], cinit, 0, 0, 0);
+    const f32x16_t zero16 = {};
+    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], zero16, 0, 0, 0);
 #pragma unroll
     for (int s = S0 + 1; s < NSTEP; ++s) {
         const u32x4 k2 = *(const u32x4 *)(lds + kbase + ((32u * s) ^ ky));
@@ -237,23 +237,23 @@ __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, un
 
 template <int NSTEP>
 __device__ inline f32x16_t qk_main(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
-                                   const bf16x8_t *qf, const f32x16_t &cinit, int zero_below) {
+                                   const bf16x8_t *qf, int zero_below) {
     switch (s_first) {
-        case 0: return qk_chain<NSTEP, 0>(lds, kbase, ky, qf, cinit, zero_below);
-        case 1: return qk_chain<NSTEP, 1>(lds, kbase, ky, qf, cinit, zero_below);
-        case 2: return qk_chain<NSTEP, 2>(lds, kbase, ky, qf, cinit, zero_below);
-        case 3: return qk_chain<NSTEP, 3>(lds, kbase, ky, qf, cinit, zero_below);
+        case 0: return qk_chain<NSTEP, 0>(lds, kbase, ky, qf, zero_below);
+        case 1: return qk_chain<NSTEP, 1>(lds, kbase, ky, qf, zero_below);
+        case 2: return qk_chain<NSTEP, 2>(lds, kbase, ky, qf, zero_below);
+        case 3: return qk_chain<NSTEP, 3>(lds, kbase, ky, qf, zero_below);
         default: break;
     }
     if constexpr (NSTEP > 4) {
         switch (s_first) {
-            case 4: return qk_chain<NSTEP, 4>(lds, kbase, ky, qf, cinit, zero_below);
-            case 5: return qk_chain<NSTEP, 5>(lds, kbase, ky, qf, cinit, zero_below);
-            case 6: return qk_chain<NSTEP, 6>(lds, kbase, ky, qf, cinit, zero_below);
-            default: return qk_chain<NSTEP, (NSTEP > 4 ? 7 : 3)>(lds, kbase, ky, qf, cinit, zero_below);
+            case 4: return qk_chain<NSTEP, 4>(lds, kbase, ky, qf, zero_below);
+            case 5: return qk_chain<NSTEP, 5>(lds, kbase, ky, qf, zero_below);
+            case 6: return qk_chain<NSTEP, 6>(lds, kbase, ky, qf, zero_below);
+            default: return qk_chain<NSTEP, (NSTEP > 4 ? 7 : 3)>(lds, kbase, ky, qf, zero_below);
         }
     }
-    return qk_chain<NSTEP, NSTEP - 1>(lds, kbase, ky, qf, cinit, zero_below);
+    return qk_chain<NSTEP, NSTEP - 1>(lds, kbase, ky, qf, zero_below);
 }
 
 template <int D>
@@ -390,23 +390,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         // boundary pairs; the second block's MFMAs overlap the first block's softmax
         f32x16_t sacc[2];
         bool live[2];
-        float m_issue = m_ref;  // reference both blocks were started from
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jb = j0 + 32 * kb;
             live[kb] = jb <= i0 + 31;
-            sacc[kb] = zero16;
-            if (!live[kb]) continue;
+            if (!live[kb]) continue;  // (a dead block's sacc is never read)
             const int dmax = i0 + 31 - jb;
             const int dmin = max(0, i0 - (jb + 31));
             const int p_lo = __builtin_popcountll(__ballot(w_lane < dmin));
             const int p_full = __builtin_popcountll(__ballot(w_lane < dmax));
             const int s_first = p_full >> 3;
             const unsigned kbase = kbase_lane + 32u * kb * (CH * 16);
-            f32x16_t cinit;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) cinit[r] = -m_issue;
-            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, cinit, p_full - 8 * s_first - koff0);
+            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, p_full - 8 * s_first - koff0);
             const bool diag = jb + 31 > i0;  // some key may follow some query
 
             // dropped terms of pairs below p_lo: every causal element of the block
@@ -460,54 +455,48 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
             const int jb = j0 + 32 * kb;
             const bool diag = jb + 31 > i0;
 
-            // accumulator = score - m_issue (log2 units); bring it to the current reference
-            if (m_issue != m_ref) {  // a rescale happened after this block was issued
-                const float adj = m_issue - m_ref;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] += adj;
-            }
             if (diag) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[kb][r] = -INFINITY;
             }
 
-            // ---- online softmax for this block (lane and lane^32 share a query)
+            // ---- online softmax for this block (lane and lane^32 share a query);
+            // scores are in log2 units, probabilities are 2^(score - m_ref)
             float bm = sacc[kb][0];
 #pragma unroll
             for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);
             bm = partner_max(bm);
-            const bool move = (kt == 0 && kb == 0) || bm > kRescale;
+            const bool move = (kt == 0 && kb == 0) || bm > m_ref + kRescale;
             if (__ballot(move)) {
-                const float shift = move ? bm : 0.f;   // new reference = m_ref + shift
-                const float corr = fast_exp2(-shift);
-                m_ref += shift;
+                const float m_new = move ? bm : m_ref;
+                const float corr = fast_exp2(m_ref - m_new);
+                m_ref = m_new;
                 l_run *= corr;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) o[db][r] *= corr;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
+                const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
+                u32x4 vwr[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) vwr[db] = *(const u32x4 *)(lt + vaddr + db * (32 * 128));
                 unsigned pw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float p0 = fast_exp2(sacc[kb][8 * t + 2 * u]);
-                    const float p1 = fast_exp2(sacc[kb][8 * t + 2 * u + 1]);
+                    const float p0 = fast_exp2(sacc[kb][8 * t + 2 * u] - m_ref);
+                    const float p1 = fast_exp2(sacc[kb][8 * t + 2 * u + 1] - m_ref);
                     pw[u] = pack_bf(p0, p1);
                     l_run = dot2_bf(pw[u], kOnesBf16x2, l_run);
                 }
                 const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
-                const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const u32x4 vw = *(const u32x4 *)(lt + vaddr + db * (32 * 128));
+                for (int db = 0; db < NDB; ++db)
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, vw), pop, o[db], 0, 0, 0);
-                }
+                        __builtin_bit_cast(bf16x8_t, vwr[db]), pop, o[db], 0, 0, 0);
             }
         }
 
