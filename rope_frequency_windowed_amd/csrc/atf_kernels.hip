@@ -622,33 +622,67 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 }
 
 // ============================================================================
-// Split-KV decode, bf16.  One workgroup = (split, b, kv head, slab of <= 8
-// query heads); its 4 waves take 64-key chunks of the split in turn.
+// Split-KV decode, bf16, on MFMA 16x16x32.  One workgroup = (split, b, kv
+// head, slab of <= 8 query heads); its 4 waves take 32-key chunks of the
+// split in turn (two groups of 16 keys).
 //
-// Scores: lane = key.  A key at distance D keeps pairs [p*(D), P); the lane
-// loads only the 16-byte pieces of its key row holding kept pairs (far keys
-// read few bytes), rotates them with cos/sin from a two-level table (per-chunk
-// coarse angle x per-lane fine angle, both built from fp64-reduced angles),
-// and takes dot products with the group's rotated queries (bf16 dot2).
-// Softmax: per head, wave-wide max/sum, online across chunks.
-// P.V: lane = pair of dims; probabilities of key pairs come from LDS.
-// Each workgroup writes (o, m, l) per head; a combine kernel merges splits.
+// Scores S^T[16 keys x 16 head slots] per group: lane (t, q) = (lane % 16,
+// lane / 16) owns key t of the group and rotates that key's pairs
+// 16s + 4q + (0..3) of each K-step s.  A key at distance D keeps pairs
+// [p*(D), P): the lane loads only the 8-byte pieces holding kept pairs (far
+// keys read few bytes) and zeroes the dropped ones; K-steps no key of the
+// chunk keeps are skipped.  cos/sin come from a two-level table (per-chunk
+// coarse angle x per-key fine angle, both from fp64-reduced angles).
+// The score output puts head t in lane column t, so each head's softmax
+// statistics are in-lane plus a max over the 4 quads.
+// P.V: O^T[16 dims x 16 heads] += V^T P^T.  The value chunk is staged in LDS
+// by direct loads (issued right after the previous chunk's P.V, so they
+// overlap this chunk's scores) and read back transposed with
+// ds_read_b64_tr_b16, whose lane mapping (16-lane groups; output lane t,
+// element c <- element t % 4 of the 8-byte read of source lane 4c + t / 4)
+// yields dim t of 4 keys per read.  A combine kernel merges the splits.
 // grid (nsplit, B*Hkv*n_slabs), block 256.
 // ============================================================================
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ inline float quad_max(float x) {  // max over lanes t, t+16, t+32, t+48
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1]));
+}
+__device__ inline float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+}
+
+// 8 bytes holding dim t of 4 consecutive keys (see the lane mapping above)
+__device__ inline u32x2 lds_read_tr16(const unsigned char *lds, unsigned byte_addr) {
+    const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(lds + byte_addr));
+    return __builtin_bit_cast(u32x2, r);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
-    constexpr int NC8 = P / 8;           // 8-pair pieces per half row
-    constexpr int NDP = D / 2;           // dim pairs
-    constexpr int KPS = 64 / NDP;        // key-pair stride per lane (1 for d=128, 2 for d=64)
+    constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
+    constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
+    constexpr int CK = 32;               // keys per wave chunk
+    constexpr int VROW = D * 2;          // bytes per value row
+    constexpr int CHV = VROW / 16;       // 16-byte chunks per value row
+    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128)
+    constexpr int VR = 1024 / VROW;      // value rows per 1 KB direct-load piece
     constexpr int H = kDecodeHeads;
-    __shared__ float2 fine[P][64];       // cos/sin(u * theta_p), u = 0..63
-    __shared__ unsigned qp[P][H];        // rotated query pairs per head (bf16x2)
+    __shared__ float2 fine[P][CK];       // cos/sin(u * theta_p), u = 0..31
     __shared__ float2 coarse[4][P];      // per wave: cos/sin((pos0 + j0) * theta_p)
-    __shared__ unsigned pbuf[4][32][H];  // per wave: key-pair probabilities per head
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[4][VBYTES];
     __shared__ int Wsh[64];
-    __shared__ float wm[4][H], wl[4][H];
+    __shared__ float wm[4][16], wl[4][16];
 
     const int split = blockIdx.x;
     const int slab = blockIdx.y % a.n_slabs;
@@ -657,44 +691,51 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const int h0 = hk * a.group + slab * H;
     const int nh = min(H, a.group - slab * H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = lane & 15, q = lane >> 4;
     const long long qpos = a.pos0 + a.S;
 
-    for (int e = tid; e < P * 64; e += 256) {
-        const int p = e >> 6, u = e & 63;
+    for (int e = tid; e < P * CK; e += 256) {
+        const int p = e / CK, u = e % CK;
         float c, s;
         rope_cos_sin(u, a.theta[p], c, s);
         fine[p][u] = make_float2(c, s);
     }
-    for (int e = tid; e < H * P; e += 256) {
-        const int hh = e / P, p = e % P;
-        unsigned w = 0u;
-        if (hh < nh) {
-            const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + hh) * D;
-            const float x = __uint_as_float((unsigned)qrow[p] << 16);
-            const float y = __uint_as_float((unsigned)qrow[p + P] << 16);
-            float c, s;
-            rope_cos_sin(qpos, a.theta[p], c, s);
-            w = pack_bf(x * c - y * s, y * c + x * s);
-        }
-        qp[p][hh] = w;
-    }
     if (tid < 64) Wsh[tid] = (tid < P) ? a.W[tid] : kWindowInf;
+
+    // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
+    // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
+    bf16x8_t qf[NSTEP];
+    {
+        const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + t) * D;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+            if (t < nh) {
+                const int pb = 16 * s + 4 * q;
+                const u32x2 lo = *(const u32x2 *)(qrow + pb);
+                const u32x2 hi = *(const u32x2 *)(qrow + P + pb);
+                unsigned r[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
+                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
+                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
+                    float c, sn;
+                    rope_cos_sin(qpos, a.theta[pb + u], c, sn);
+                    r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
+                }
+                w = (u32x4){r[0], r[1], r[2], r[3]};
+            }
+            qf[s] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
     __syncthreads();
 
     const int ks = a.split_start[split];
     const int ke = min(a.split_start[split + 1], a.S);
     const unsigned short *kbase = (const unsigned short *)a.k + (long long)bk * a.S * D;
-    const unsigned short *vbase = (const unsigned short *)a.v + (long long)bk * a.S * D;
-
-    float m_h[H], l_h[H], o0[H], o1[H];
-#pragma unroll
-    for (int hh = 0; hh < H; ++hh) {
-        m_h[hh] = -INFINITY;
-        l_h[hh] = 0.f;
-        o0[hh] = 0.f;
-        o1[hh] = 0.f;
-    }
-    unsigned long long skipped = 0;
+    const unsigned char *vbase = (const unsigned char *)a.v + (long long)bk * a.S * VROW;
+    unsigned char *vb = vbuf[wave];
 
     // p*(delta) = #{p < P-1 : W_p < delta}, by binary lifting over the sorted table
     auto pstar = [&](int delta) {
@@ -705,7 +746,42 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         return c;
     };
 
-    for (int j0 = ks + wave * 64; j0 < ke; j0 += 256) {
+    // Value rows are staged with 16-byte chunks swizzled: row r, chunk c at
+    // byte r*VROW + ((c ^ vsw(r)) << 4), vsw(r) = 2 (r mod CHV/2), so the
+    // transposed reads of a 16-lane group (4 rows x 32 bytes) hit distinct
+    // banks.  Direct-load piece m (1 KB, VR rows): lane l lands at byte
+    // 16 l, i.e. row VR m + l / CHV, physical chunk l % CHV.
+    const int vlr = lane / CHV;
+    auto vsw = [](int r) { return 2 * (r % (CHV / 2)); };
+    auto stage_values = [&](int j0) {
+        const int nrow = min(CK, ke - j0);  // rows past the split end repeat its last row
+#pragma unroll
+        for (int m = 0; m < VBYTES / 1024; ++m) {
+            const int row = VR * m + vlr;
+            const int c = (lane % CHV) ^ vsw(row);
+            const int grow = j0 + min(row, nrow - 1);
+            lds_dma16(vbase + (long long)grow * VROW + c * 16, vb + m * 1024);
+        }
+    };
+    // this lane's transposed-read byte address for output block db, key group hh
+    auto vtr_addr = [&](int db, int hh) {
+        const int row = 16 * hh + 4 * q + (t >> 2);
+        const int col = 32 * db + 8 * (t & 3);  // byte column
+        return (unsigned)(row * VROW + ((((col >> 4) ^ vsw(row)) << 4) | (col & 15)));
+    };
+
+    f32x4_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    constexpr float kRescale = 8.f;
+    constexpr unsigned kOnesBf16x2 = 0x3f803f80u;
+    float m_ref = 0.f, l_run = 0.f;
+    bool first = true;
+    unsigned long long skipped = 0;
+
+    int j0 = ks + wave * CK;
+    if (j0 < ke) stage_values(j0);
+    for (; j0 < ke; j0 += 4 * CK) {
         if (lane < P) {
             float c, s;
             rope_cos_sin(a.pos0 + j0, a.theta[lane], c, s);
@@ -715,111 +791,102 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        const int j = j0 + lane;
-        const bool valid = j < ke;
-        const int ps = valid ? pstar(a.S - j) : P;
-        if (valid) skipped += (unsigned long long)ps * (unsigned)nh;
-        const int pmin = pstar(a.S - min(j0 + 63, ke - 1));  // fewest dropped pairs in the chunk
-
-        float sc[H];
+        // fewest dropped pairs in the chunk: its nearest key
+        const int s_min = pstar(a.S - min(j0 + CK - 1, ke - 1)) >> 4;
+        f32x4_t sc[2];
 #pragma unroll
-        for (int hh = 0; hh < H; ++hh) sc[hh] = 0.f;
-        const unsigned short *krow = kbase + (long long)j * D;
-        for (int c8 = pmin >> 3; c8 < NC8; ++c8) {
-            u32x4 lo = (u32x4){0u, 0u, 0u, 0u}, hi = lo;
-            if (8 * c8 + 8 > ps) {
-                lo = *(const u32x4 *)(krow + 8 * c8);
-                hi = *(const u32x4 *)(krow + P + 8 * c8);
-            }
-            const unsigned lw[4] = {lo.x, lo.y, lo.z, lo.w};
-            const unsigned hw[4] = {hi.x, hi.y, hi.z, hi.w};
+        for (int g = 0; g < 2; ++g) {
+            const int u = 16 * g + t;  // key offset in the chunk
+            const int j = j0 + u;
+            const bool valid = j < ke;
+            const int ps = valid ? pstar(a.S - j) : P;
+            if (valid && q == 0) skipped += (unsigned long long)ps * (unsigned)nh;
+            const unsigned short *krow = kbase + (long long)j * D;
+            f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int p = 8 * c8 + u;
-                const float x = (u & 1) ? bf_hi(lw[u >> 1]) : bf_lo(lw[u >> 1]);
-                const float y = (u & 1) ? bf_hi(hw[u >> 1]) : bf_lo(hw[u >> 1]);
-                const float2 f = fine[p][lane];
-                const float2 cc = coarse[wave][p];
-                const float cs = f.x * cc.x - f.y * cc.y;
-                const float sn = f.y * cc.x + f.x * cc.y;
-                const unsigned kp = (p < ps) ? 0u : pack_bf(x * cs - y * sn, y * cs + x * sn);
-                const u32x4 qa = *(const u32x4 *)&qp[p][0];
-                const u32x4 qb = *(const u32x4 *)&qp[p][4];
-                sc[0] = dot2_bf(kp, qa.x, sc[0]);
-                sc[1] = dot2_bf(kp, qa.y, sc[1]);
-                sc[2] = dot2_bf(kp, qa.z, sc[2]);
-                sc[3] = dot2_bf(kp, qa.w, sc[3]);
-                sc[4] = dot2_bf(kp, qb.x, sc[4]);
-                sc[5] = dot2_bf(kp, qb.y, sc[5]);
-                sc[6] = dot2_bf(kp, qb.z, sc[6]);
-                sc[7] = dot2_bf(kp, qb.w, sc[7]);
+            for (int s = 0; s < NSTEP; ++s) {
+                if (s < s_min) continue;
+                const int pb = 16 * s + 4 * q;
+                u32x2 lo = (u32x2){0u, 0u}, hi = lo;
+                if (pb + 4 > ps) {
+                    lo = *(const u32x2 *)(krow + pb);
+                    hi = *(const u32x2 *)(krow + P + pb);
+                }
+                unsigned r[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int p = pb + w;
+                    const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
+                    const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
+                    const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
+                    const float2 f = fine[p][u];
+                    const float2 cc = coarse[wave][p];
+                    const float cs = f.x * cc.x - f.y * cc.y;
+                    const float sn = f.y * cc.x + f.x * cc.y;
+                    r[w] = (p < ps) ? 0u : pack_bf(x * cs - y * sn, y * cs + x * sn);
+                }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, (u32x4){r[0], r[1], r[2], r[3]}), qf[s], acc, 0, 0, 0);
             }
+            // rows of acc are keys 4q + (0..3) of the group; drop keys past the split
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (j0 + 16 * g + 4 * q + i >= ke) acc[i] = -INFINITY;
+            sc[g] = acc;
         }
 
+        // online softmax per head slot t (log2 units, lazy reference)
+        float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        bm = quad_max(bm);
+        const bool move = first || bm > m_ref + kRescale;
+        first = false;
+        if (__ballot(move)) {
+            const float m_new = move ? bm : m_ref;
+            const float corr = fast_exp2(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= corr;
 #pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-            const float x = valid ? sc[hh] * a.scale_log2 : -INFINITY;
-            const float m_new = fmaxf(m_h[hh], wave_max(x));
-            const float corr = fast_exp2(m_h[hh] - m_new);
-            const float pr = fast_exp2(x - m_new);
-            l_h[hh] = l_h[hh] * corr + wave_sum(pr);
-            o0[hh] *= corr;
-            o1[hh] *= corr;
-            m_h[hh] = m_new;
-            const float pn = __shfl_down(pr, 1);
-            if (!(lane & 1)) pbuf[wave][lane >> 1][hh] = pack_bf(pr, pn);
+            for (int db = 0; db < NDB; ++db) o[db] *= corr;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        unsigned pw[4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            pw[2 * g] = pack_bf(fast_exp2(sc[g][0] - m_ref), fast_exp2(sc[g][1] - m_ref));
+            pw[2 * g + 1] = pack_bf(fast_exp2(sc[g][2] - m_ref), fast_exp2(sc[g][3] - m_ref));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+
+        // P.V: values of this chunk have landed in LDS
+        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        const int d2 = lane % NDP;
-        for (int kp = lane / NDP; kp < 32; kp += KPS) {
-            const int ja = j0 + 2 * kp;
-            unsigned w0 = 0u, w1 = 0u;
-            if (ja < ke) w0 = *(const unsigned *)(vbase + (long long)ja * D + 2 * d2);
-            if (ja + 1 < ke) w1 = *(const unsigned *)(vbase + (long long)(ja + 1) * D + 2 * d2);
-            const unsigned va = __builtin_amdgcn_perm(w1, w0, 0x05040100u);  // (v[ja][2d2], v[ja+1][2d2])
-            const unsigned vb = __builtin_amdgcn_perm(w1, w0, 0x07060302u);  // (v[ja][2d2+1], v[ja+1][2d2+1])
-            const u32x4 pa = *(const u32x4 *)&pbuf[wave][kp][0];
-            const u32x4 pb = *(const u32x4 *)&pbuf[wave][kp][4];
-            const unsigned pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) {
-                o0[hh] = dot2_bf(pv[hh], va, o0[hh]);
-                o1[hh] = dot2_bf(pv[hh], vb, o1[hh]);
-            }
+        for (int db = 0; db < NDB; ++db) {
+            const u32x2 v0 = lds_read_tr16(vb, vtr_addr(db, 0));
+            const u32x2 v1 = lds_read_tr16(vb, vtr_addr(db, 1));
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}), pop, o[db], 0, 0, 0);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_s_waitcnt(0);  // transposed reads done before the buffer is refilled
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (j0 + 4 * CK < ke) stage_values(j0 + 4 * CK);
     }
 
-    // lanes sharing a dim pair (d = 64) hold disjoint key pairs: add them up
-    if (KPS == 2) {
-#pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-            o0[hh] += __shfl_xor(o0[hh], 32);
-            o1[hh] += __shfl_xor(o1[hh], 32);
-        }
-    }
-
-    // ---- merge the 4 waves (reuses the fine table's LDS) and write partials
+    // ---- merge the 4 waves (reuses the value buffers) and write partials
+    l_run = quad_sum(l_run);
     __syncthreads();
-    float *wo = (float *)&fine[0][0];  // [4][H][D]
-    if (lane < NDP) {
+    float *wo = (float *)&vbuf[0][0];  // [4][H][D]
+    if (t < nh) {
 #pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-            wo[(wave * H + hh) * D + 2 * lane] = o0[hh];
-            wo[(wave * H + hh) * D + 2 * lane + 1] = o1[hh];
-        }
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wo[(wave * H + t) * D + 16 * db + 4 * q + i] = o[db][i];
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int hh = 0; hh < H; ++hh) {
-            wm[wave][hh] = m_h[hh];
-            wl[wave][hh] = l_h[hh];
-        }
+    if (q == 0) {
+        wm[wave][t] = first ? -INFINITY : m_ref;  // a wave without keys contributes nothing
+        wl[wave][t] = l_run;
     }
     __syncthreads();
     for (int e = tid; e < nh * (D + 2); e += 256) {
