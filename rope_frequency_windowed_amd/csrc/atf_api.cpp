@@ -98,8 +98,10 @@ int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S) {
     const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
     const int64_t units = (int64_t)B * Hkv * n_slabs;
     const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
-    // aim for ~2048 workgroups (8 per CU on 256 CUs), at least one chunk each
-    int64_t ns = (2048 + units - 1) / units;
+    // aim for one round of resident workgroups: the kernel's registers allow
+    // 2 workgroups (8 waves) per CU, x 256 CUs = 512; byte-balanced splits then
+    // finish together.  At least one chunk per split.
+    int64_t ns = (512 + units - 1) / units;
     ns = std::min<int64_t>(ns, kMaxSplits);
     ns = std::min<int64_t>(ns, nchunks);
     return (int)std::max<int64_t>(ns, 1);
@@ -110,9 +112,23 @@ size_t decode_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d)
     return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
-// Splits of equal ALGORITHMIC bytes: a key at distance D costs
-// 4 (P - p*(D)) bytes of kept key pairs plus 2d bytes of value, so far chunks
-// (fewer kept pairs) are longer.  Boundaries fall on 64-key chunks.
+// Algorithmic bytes of keys [0, j) for a query at distance S - j' from key j':
+// each key costs 2d bytes of value plus 4 bytes per kept pair.  Pair p (finite
+// W_p) is dropped for keys with S - j' > W_p, i.e. j' < S - W_p, so the dropped
+// pair-keys below j are sum_p min(j, max(0, S - W_p)).  O(P) per evaluation.
+double decode_prefix_bytes(int64_t j, int64_t S, int P, int d, const int *Wi) {
+    double dropped = 0.0;
+    for (int p = 0; p < P - 1; ++p) {
+        const int64_t lim = S - (int64_t)Wi[p];
+        if (lim > 0) dropped += (double)std::min(j, lim);
+    }
+    return (double)j * (2.0 * d + 4.0 * P) - 4.0 * dropped;
+}
+
+// Splits of equal ALGORITHMIC bytes: far keys (fewer kept pairs) are cheaper,
+// so far splits hold more keys.  Boundaries fall on 64-key chunks and are found
+// by binary search on the closed-form prefix, so planning costs
+// O(nsplit * P * log(S)) host work however long the cache is.
 void plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, const int *Wi,
                  DecodePlan &plan) {
     const int P = d / 2;
@@ -120,28 +136,21 @@ void plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, const
     plan.n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
     plan.nsplit = decode_nsplit(B, Hq, Hkv, S);
     const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
-    std::vector<double> cum((size_t)nchunks + 1, 0.0);
-    for (int64_t c = 0; c < nchunks; ++c) {
-        double bytes = 0.0;
-        const int64_t jend = std::min<int64_t>(S, (c + 1) * kKeyTile);
-        for (int64_t j = c * kKeyTile; j < jend; ++j) {
-            const int64_t delta = S - j;
-            int ps = 0;
-            while (ps < P - 1 && (int64_t)Wi[ps] < delta) ++ps;
-            bytes += 4.0 * (P - ps) + 2.0 * d;
-        }
-        cum[(size_t)c + 1] = cum[(size_t)c] + bytes;
-    }
-    const double total = cum[(size_t)nchunks];
+    auto cum = [&](int64_t c) { return decode_prefix_bytes(std::min(S, c * kKeyTile), S, P, d, Wi); };
+    const double total = cum(nchunks);
     plan.starts[0] = 0;
-    int64_t c = 0;
     for (int s = 1; s < plan.nsplit; ++s) {
         const double target = total * s / plan.nsplit;
-        while (c < nchunks && cum[(size_t)c] < target) ++c;
+        // smallest chunk index c with cum(c) >= target (cum is increasing)
+        int64_t lo = 0, hi = nchunks;
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (cum(mid) < target) lo = mid + 1; else hi = mid;
+        }
         // keep every split non-empty
-        const int64_t lo = plan.starts[s - 1] / kKeyTile + 1;
-        const int64_t hi = nchunks - (plan.nsplit - s);
-        const int64_t cc = std::max(lo, std::min(c, hi));
+        const int64_t first = plan.starts[s - 1] / kKeyTile + 1;
+        const int64_t last = nchunks - (plan.nsplit - s);
+        const int64_t cc = std::max(first, std::min(lo, last));
         plan.starts[s] = (int)(cc * kKeyTile);
     }
     plan.starts[plan.nsplit] = (int)(nchunks * kKeyTile);

@@ -680,8 +680,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int H = kDecodeHeads;
     __shared__ float2 fine[P][CK];       // cos/sin(u * theta_p), u = 0..31
     __shared__ float2 coarse[4][P];      // per wave: cos/sin((pos0 + j0) * theta_p)
+    __shared__ float2 stride_cs[P];      // cos/sin(4 * CK * theta_p): one wave step
     __shared__ __attribute__((aligned(1024))) unsigned char vbuf[4][VBYTES];
-    __shared__ int Wsh[64];
     __shared__ float wm[4][16], wl[4][16];
 
     const int split = blockIdx.x;
@@ -700,7 +700,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         rope_cos_sin(u, a.theta[p], c, s);
         fine[p][u] = make_float2(c, s);
     }
-    if (tid < 64) Wsh[tid] = (tid < P) ? a.W[tid] : kWindowInf;
+    if (tid < P) {
+        float c, s;
+        rope_cos_sin(4 * CK, a.theta[tid], c, s);
+        stride_cs[tid] = make_float2(c, s);
+    }
+    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
 
     // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
     // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
@@ -737,32 +742,26 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const unsigned char *vbase = (const unsigned char *)a.v + (long long)bk * a.S * VROW;
     unsigned char *vb = vbuf[wave];
 
-    // p*(delta) = #{p < P-1 : W_p < delta}, by binary lifting over the sorted table
-    auto pstar = [&](int delta) {
-        int c = 0;
-#pragma unroll
-        for (int st = 32; st > 0; st >>= 1)
-            if (c + st <= P - 1 && Wsh[c + st - 1] < delta) c += st;
-        return c;
-    };
-
     // Value rows are staged with 16-byte chunks swizzled: row r, chunk c at
     // byte r*VROW + ((c ^ vsw(r)) << 4), vsw(r) = 2 (r mod CHV/2), so the
     // transposed reads of a 16-lane group (4 rows x 32 bytes) hit distinct
-    // banks.  Direct-load piece m (1 KB, VR rows): lane l lands at byte
-    // 16 l, i.e. row VR m + l / CHV, physical chunk l % CHV.
+    // banks.  The chunk is prefetched into registers one chunk ahead (lane l
+    // of 1 KB piece m holds LDS bytes 1024 m + 16 l: row VR m + l / CHV,
+    // physical chunk l % CHV) and written to LDS when its turn comes.
+    constexpr int NVP = VBYTES / 1024;  // pieces per chunk
     const int vlr = lane / CHV;
     auto vsw = [](int r) { return 2 * (r % (CHV / 2)); };
-    auto stage_values = [&](int j0) {
-        const int nrow = min(CK, ke - j0);  // rows past the split end repeat its last row
-#pragma unroll
-        for (int m = 0; m < VBYTES / 1024; ++m) {
-            const int row = VR * m + vlr;
-            const int c = (lane % CHV) ^ vsw(row);
-            const int grow = j0 + min(row, nrow - 1);
-            lds_dma16(vbase + (long long)grow * VROW + c * 16, vb + m * 1024);
-        }
-    };
+    u32x4 vreg[NVP];
+#define DEC_LOAD_V(jc_)                                                                 \
+    {                                                                                 \
+        const int nrow_ = min(CK, ke - (jc_));  /* rows past the split repeat its last row */ \
+        _Pragma("unroll") for (int m = 0; m < NVP; ++m) {                             \
+            const int row_ = VR * m + vlr;                                            \
+            const int c_ = (lane % CHV) ^ vsw(row_);                                  \
+            const int grow_ = (jc_) + min(row_, nrow_ - 1);                           \
+            vreg[m] = *(const u32x4 *)(vbase + (long long)grow_ * VROW + c_ * 16);    \
+        }                                                                             \
+    }
     // this lane's transposed-read byte address for output block db, key group hh
     auto vtr_addr = [&](int db, int hh) {
         const int row = 16 * hh + 4 * q + (t >> 2);
@@ -779,38 +778,102 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     bool first = true;
     unsigned long long skipped = 0;
 
+    // Per-chunk key bookkeeping.  Dropped pairs per key: the chunk's nearest
+    // key has the fewest (p_near, one ballot); farther keys add the few
+    // windows that fall inside the chunk's distance range.
+#define DEC_CHUNK_KEYS(jc_, smin_, ps0_, ps1_)                                          \
+    {                                                                                 \
+        const int d_near_ = a.S - min((jc_) + CK - 1, ke - 1);                        \
+        const int d_far_ = a.S - (jc_);                                               \
+        const int p_near_ = __builtin_popcountll(__ballot(w_lane < d_near_));         \
+        smin_ = p_near_ >> 4;                                                         \
+        ps0_ = p_near_;                                                               \
+        ps1_ = p_near_;                                                               \
+        for (int pp = p_near_; pp < P - 1; ++pp) {                                    \
+            const int wpp = __builtin_amdgcn_readlane(w_lane, pp);                    \
+            if (wpp >= d_far_) break;                                                 \
+            ps0_ += (wpp < a.S - ((jc_) + t)) ? 1 : 0;                                \
+            ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;                           \
+        }                                                                             \
+        if ((jc_) + t >= ke) ps0_ = P;                                                \
+        if ((jc_) + 16 + t >= ke) ps1_ = P;                                           \
+    }
+    // Key pieces of the last two K-steps (the only ones far keys keep) are
+    // loaded one chunk ahead into registers; nearer steps load on use.  Every
+    // load is issued unconditionally (fixed vmcnt bookkeeping, no divergent
+    // branches): a piece the lane does not need reads the key row's last
+    // 8 bytes of each half (pairs P-4..P-1, never cut, so another lane fetches
+    // the same sectors anyway), and the per-pair mask zeroes it.
+    constexpr int SPRE = (NSTEP >= 2) ? NSTEP - 2 : 0;
+#define DEC_LOAD_K(jc_, ps0_, ps1_)                                                     \
+    {                                                                                 \
+        _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
+            const int psg_ = g ? (ps1_) : (ps0_);                                     \
+            const unsigned short *kr_ = kbase + (long long)min((jc_) + 16 * g + t, ke - 1) * D; \
+            _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i) {                \
+                const int pb_ = 16 * (SPRE + i) + 4 * q;                              \
+                const int off_ = (pb_ + 4 > psg_) ? pb_ : (P - 4);                    \
+                klo[g][i] = *(const u32x2 *)(kr_ + off_);                             \
+                khi[g][i] = *(const u32x2 *)(kr_ + P + off_);                         \
+            }                                                                         \
+        }                                                                             \
+    }
+
     int j0 = ks + wave * CK;
-    if (j0 < ke) stage_values(j0);
-    for (; j0 < ke; j0 += 4 * CK) {
+    int s_min = 0, ps0 = P, ps1 = P;
+    u32x2 klo[2][NSTEP - SPRE], khi[2][NSTEP - SPRE];
+    if (j0 < ke) {
+        DEC_LOAD_V(j0);
+        DEC_CHUNK_KEYS(j0, s_min, ps0, ps1);
+        DEC_LOAD_K(j0, ps0, ps1);
+    }
+    // coarse angle of this lane's pair at the wave's current chunk start:
+    // exact every 16 chunks, advanced by one wave stride in between
+    float2 cs_lane = make_float2(1.f, 0.f), cs_step = make_float2(1.f, 0.f);
+    if (lane < P) cs_step = stride_cs[lane];
+    for (int it = 0; j0 < ke; j0 += 4 * CK, ++it) {
+        const int jn = j0 + 4 * CK;
+        // this chunk's values to LDS (the previous chunk's transposed reads,
+        // earlier in this wave's LDS order, are done with the buffer), then
+        // the next chunk's values into the freed registers
+#pragma unroll
+        for (int m = 0; m < NVP; ++m) *(u32x4 *)(vb + m * 1024 + lane * 16) = vreg[m];
+        if (jn < ke) DEC_LOAD_V(jn);
         if (lane < P) {
-            float c, s;
-            rope_cos_sin(a.pos0 + j0, a.theta[lane], c, s);
-            coarse[wave][lane] = make_float2(c, s);
+            if ((it & 15) == 0) {
+                float c, s;
+                rope_cos_sin(a.pos0 + j0, a.theta[lane], c, s);
+                cs_lane = make_float2(c, s);
+            } else {
+                cs_lane = make_float2(cs_lane.x * cs_step.x - cs_lane.y * cs_step.y,
+                                      cs_lane.y * cs_step.x + cs_lane.x * cs_step.y);
+            }
+            coarse[wave][lane] = cs_lane;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // fewest dropped pairs in the chunk: its nearest key
-        const int s_min = pstar(a.S - min(j0 + CK - 1, ke - 1)) >> 4;
         f32x4_t sc[2];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int u = 16 * g + t;  // key offset in the chunk
-            const int j = j0 + u;
-            const bool valid = j < ke;
-            const int ps = valid ? pstar(a.S - j) : P;
-            if (valid && q == 0) skipped += (unsigned long long)ps * (unsigned)nh;
-            const unsigned short *krow = kbase + (long long)j * D;
+            const int ps = g ? ps1 : ps0;
+            if (q == 0 && ps < P) skipped += (unsigned long long)ps * (unsigned)nh;
+            const unsigned short *krow = kbase + (long long)min(j0 + u, ke - 1) * D;
             f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < NSTEP; ++s) {
                 if (s < s_min) continue;
                 const int pb = 16 * s + 4 * q;
-                u32x2 lo = (u32x2){0u, 0u}, hi = lo;
-                if (pb + 4 > ps) {
-                    lo = *(const u32x2 *)(krow + pb);
-                    hi = *(const u32x2 *)(krow + P + pb);
+                u32x2 lo, hi;
+                if (s >= SPRE) {
+                    lo = klo[g][s - SPRE];
+                    hi = khi[g][s - SPRE];
+                } else {
+                    const int off = (pb + 4 > ps) ? pb : (P - 4);
+                    lo = *(const u32x2 *)(krow + off);
+                    hi = *(const u32x2 *)(krow + P + off);
                 }
                 unsigned r[4];
 #pragma unroll
@@ -833,6 +896,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i)
                 if (j0 + 16 * g + 4 * q + i >= ke) acc[i] = -INFINITY;
             sc[g] = acc;
+        }
+
+        // next chunk's keys: bookkeeping and the prefetched key pieces
+        if (jn < ke) {
+            DEC_CHUNK_KEYS(jn, s_min, ps0, ps1);
+            DEC_LOAD_K(jn, ps0, ps1);
         }
 
         // online softmax per head slot t (log2 units, lazy reference)
@@ -859,9 +928,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
         const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
 
-        // P.V: values of this chunk have landed in LDS
-        __builtin_amdgcn_s_waitcnt(0);
+        // P.V on this chunk's values (written to LDS by this wave above)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             const u32x2 v0 = lds_read_tr16(vb, vtr_addr(db, 0));
@@ -869,10 +939,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}), pop, o[db], 0, 0, 0);
         }
-        __builtin_amdgcn_s_waitcnt(0);  // transposed reads done before the buffer is refilled
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        if (j0 + 4 * CK < ke) stage_values(j0 + 4 * CK);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+#undef DEC_CHUNK_KEYS
+#undef DEC_LOAD_K
+#undef DEC_LOAD_V
 
     // ---- merge the 4 waves (reuses the value buffers) and write partials
     l_run = quad_sum(l_run);

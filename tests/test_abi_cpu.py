@@ -125,7 +125,7 @@ def test_workspace_sizes(lib):
     assert atf.atf_prefill_workspace_bytes(1, 1, 256, 64, atf.ATF_F32) == 256
     assert atf.atf_prefill_workspace_bytes(1, 1, 256, 96, atf.ATF_BF16) == 0
     ws = atf.atf_decode_workspace_bytes(8, 28, 4, 262144, 128)
-    assert ws == 256 + 8 * 28 * 64 * 130 * 4
+    assert ws == 256 + 8 * 28 * 16 * 130 * 4  # 512 workgroups over 32 (sequence, kv head) units
     assert atf.atf_decode_workspace_bytes(1, 1, 1, 10, 128) == 256 + 1 * 1 * 1 * 130 * 4
     assert atf.atf_decode_workspace_bytes(1, 3, 2, 10, 128) == 0
 
