@@ -34,6 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
 KERNEL_SRC = os.path.join(ROOT, "rope_frequency_windowed_amd", "csrc", "atf_kernels.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_counters.txt")
+DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kv262144_counters.txt")
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
@@ -63,17 +64,18 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic():
-    """Counter-measured HBM bytes per prefill-attention launch, if the summary
+def read_traffic(path=COUNTERS_FILE):
+    """Counter-measured HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what the same counter reads for a 1 GiB copy), if the summary
     was taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(COUNTERS_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
-                vals[k.strip()] = v.strip()
+                vals[k.strip()] = v.split()[0] if v.split() else ""
     if vals.get("kernel_source_sha256_16") != source_hash():
         return None
     try:
@@ -238,7 +240,8 @@ def main():
         gbs = nbytes / (dec_ms * 1e-3) / 1e9
         res["decode"] = {"value": gbs, "unit": "GB/s", "ms": dec_ms, "tok_per_s": DECODE["B"] / (dec_ms * 1e-3),
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+                                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                                      "traffic": read_traffic(DECODE_COUNTERS_FILE)}}
         config["decode"] = dict(DECODE)
         log("decode: %.3f ms, %.3g algorithmic bytes, %.0f GB/s (%.1f%% of HBM peak)"
             % (dec_ms, nbytes, gbs, 100 * gbs / HBM_PEAK_GBS))
