@@ -174,8 +174,8 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 //
 // Workgroup = 4 waves = 128 queries of one (b, h); wave w owns 32 queries.
 // Key tiles of 64 keys stream global -> LDS with direct LDS loads
-// (global_load_lds_dwordx4, no staging registers), double-buffered, one
-// barrier per tile.  Per tile each wave computes two 32x32 score blocks
+// (buffer_load_dwordx4 ... lds: no staging registers, the tile base advances
+// in scalar registers), double-buffered, one barrier per tile.  Per tile each wave computes two 32x32 score blocks
 // S^T = K' Q'^T (keys on MFMA rows, queries on columns: a lane holds 16 keys
 // of one query, its partner lane^32 the other 16, so softmax row statistics
 // need one lane swap), then O^T += V^T P^T.  Both blocks' score MFMAs are
@@ -192,8 +192,9 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // added element by element where the distance is within W_p.  Dropped terms
 // are counted exactly.
 //
-// Scores come out in log2 units: q' is pre-scaled by log2(e)/sqrt(d), so a
-// probability is 2^(score - m_ref) for the running reference m_ref.
+// Scores come out in log2 units and already shifted by the softmax reference:
+// q' is pre-scaled by log2(e)/sqrt(d), and each score chain starts with a
+// rank-1 MFMA that puts -m_ref in every element, so a probability is 2^score.
 // ============================================================================
 
 __device__ inline float partner_max(float x) {
@@ -213,12 +214,24 @@ __device__ inline void lds_dma16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds(src, (lds_void_t *)dst, 16, 0, 0);
 }
 
+// Buffer resource for `bytes` bytes at a wave-uniform base (raw, unswizzled);
+// reads at offsets >= bytes return zero instead of touching memory.
+__device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Same as lds_dma16, addressed as buffer base (SGPRs) + per-lane byte offset,
+// so advancing the base costs no vector instructions.
+__device__ inline void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, 0, 0, 0);
+}
+
 // One block's main score chain starting at K-step S0 (compile time).
 // kaddr(s) = kbase + ((32 s) ^ ky): the swizzled byte address of this lane's
 // 16 key dims of step s.
 template <int NSTEP, int S0>
 __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, unsigned ky,
-                                    const bf16x8_t *qf, int zero_below) {
+                                    const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b) {
     u32x4 kw = *(const u32x4 *)(lds + kbase + ((32u * S0) ^ ky));
     // words (pairs) of the first step below p_full are dropped or boundary
     kw.x = (0 < zero_below) ? 0u : kw.x;
@@ -226,7 +239,11 @@ __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, un
     kw.z = (2 < zero_below) ? 0u : kw.z;
     kw.w = (3 < zero_below) ? 0u : kw.w;
     const f32x16_t zero16 = {};
-    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], zero16, 0, 0, 0);
+    // -m_ref of each query column in every element: one rank-1 product (a column
+    // of ones times the row of -m_ref), so the scores leave the chain already
+    // shifted by the softmax reference
+    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, negm_b, zero16, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], acc, 0, 0, 0);
 #pragma unroll
     for (int s = S0 + 1; s < NSTEP; ++s) {
         const u32x4 k2 = *(const u32x4 *)(lds + kbase + ((32u * s) ^ ky));
@@ -237,23 +254,32 @@ __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, un
 
 template <int NSTEP>
 __device__ inline f32x16_t qk_main(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
-                                   const bf16x8_t *qf, int zero_below) {
+                                   const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b) {
+#define ATF_CHAIN(s0_) qk_chain<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b)
     switch (s_first) {
-        case 0: return qk_chain<NSTEP, 0>(lds, kbase, ky, qf, zero_below);
-        case 1: return qk_chain<NSTEP, 1>(lds, kbase, ky, qf, zero_below);
-        case 2: return qk_chain<NSTEP, 2>(lds, kbase, ky, qf, zero_below);
-        case 3: return qk_chain<NSTEP, 3>(lds, kbase, ky, qf, zero_below);
+        case 0: return ATF_CHAIN(0);
+        case 1: return ATF_CHAIN(1);
+        case 2: return ATF_CHAIN(2);
+        case 3: return ATF_CHAIN(3);
         default: break;
     }
     if constexpr (NSTEP > 4) {
         switch (s_first) {
-            case 4: return qk_chain<NSTEP, 4>(lds, kbase, ky, qf, zero_below);
-            case 5: return qk_chain<NSTEP, 5>(lds, kbase, ky, qf, zero_below);
-            case 6: return qk_chain<NSTEP, 6>(lds, kbase, ky, qf, zero_below);
-            default: return qk_chain<NSTEP, (NSTEP > 4 ? 7 : 3)>(lds, kbase, ky, qf, zero_below);
+            case 4: return ATF_CHAIN(4);
+            case 5: return ATF_CHAIN(5);
+            case 6: return ATF_CHAIN(6);
+            default: return ATF_CHAIN((NSTEP > 4 ? 7 : 3));
         }
     }
-    return qk_chain<NSTEP, NSTEP - 1>(lds, kbase, ky, qf, zero_below);
+    return ATF_CHAIN(NSTEP - 1);
+#undef ATF_CHAIN
+}
+
+// Smallest bf16 value >= x (finite x): the softmax reference is kept exactly
+// representable in bf16 so the score MFMA can subtract it.
+__device__ inline float bf16_ceil(float x) {
+    const unsigned u = __float_as_uint(x);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0xffff0000u) : ((u + 0xffffu) & 0xffff0000u));
 }
 
 template <int D>
@@ -340,18 +366,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         const int vrow = kbyte / 128;
         v_goff[n] = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
     }
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    // a key chunk below c_min is not fetched: its offset is past the buffer's end
+#define ATF_KOFF(n_, cmin_) ((k_chunk[n_] >= (cmin_)) ? k_goff[n_] : KT_BYTES)
 #define ATF_TILE_LOAD(kt_, buf_)                                                           \
     {                                                                                      \
         const int j0_ = (kt_) * kKeyTile;                                                  \
         const int dmin_wg_ = max(0, qt * kQueryTile - (j0_ + kKeyTile - 1));               \
         const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
-        const unsigned char *ks_ = kg + (long long)j0_ * (D * 2);                          \
-        const unsigned char *vs_ = vg + (long long)j0_ * (D * 2);                          \
-        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave * (NLD * 1024);              \
+        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
+        const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
+        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * (NLD * 1024);            \
         _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
-            if (k_chunk[n] >= c_min_)                                                      \
-                lds_dma16(ks_ + k_goff[n], lk_ + n * 1024);                                \
-            lds_dma16(vs_ + v_goff[n], lk_ + KT_BYTES + n * 1024);                         \
+            lds_dma16_buf(kr_, ATF_KOFF(n, c_min_), lk_ + n * 1024);                       \
+            lds_dma16_buf(vr_, v_goff[n], lk_ + KT_BYTES + n * 1024);                      \
         }                                                                                  \
     }
 
@@ -360,12 +388,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    // Reference max m_ref (log2 units) and running sum.  m_ref moves only when
-    // a block's max exceeds it by more than kRescale (and at the first block),
-    // so probabilities stay below 2^kRescale and the O rescale is rare.
-    constexpr float kRescale = 8.f;
+    // Softmax reference m_ref (log2 units, a bf16 value) and running sum.  The
+    // score MFMAs subtract m_ref, so a probability is 2^score.  m_ref moves
+    // only at the first block and when a lane's sum over a block's 16 keys
+    // exceeds kSumLimit (some probability above kSumLimit/16, or an overflow):
+    // then the block's exact max becomes the reference and the block is redone.
+    // Probabilities therefore stay below kSumLimit and the O rescale is rare.
+    constexpr float kSumLimit = 4096.f;
     constexpr unsigned kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
     float m_ref = 0.f, l_run = 0.f;
+    bool first = true;
+    // rank-1 operands of the reference: element k = 0 of lanes 0..31 (A: ones
+    // for every key row; B: -m_ref of the lane's query column), zeros elsewhere
+    const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, (u32x4){half ? 0u : 0x3f80u, 0u, 0u, 0u});
+    bf16x8_t negm_b = __builtin_bit_cast(bf16x8_t, (u32x4){0u, 0u, 0u, 0u});
     unsigned long long skipped = 0;
     const f32x16_t zero16 = {};
     const int koff0 = 4 * half;
@@ -401,7 +437,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
             const int p_full = __builtin_popcountll(__ballot(w_lane < dmax));
             const int s_first = p_full >> 3;
             const unsigned kbase = kbase_lane + 32u * kb * (CH * 16);
-            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, p_full - 8 * s_first - koff0);
+            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, p_full - 8 * s_first - koff0, ones_a, negm_b);
             const bool diag = jb + 31 > i0;  // some key may follow some query
 
             // dropped terms of pairs below p_lo: every causal element of the block
@@ -462,41 +498,59 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
             }
 
             // ---- online softmax for this block (lane and lane^32 share a query);
-            // scores are in log2 units, probabilities are 2^(score - m_ref)
-            float bm = sacc[kb][0];
+            // scores are in log2 units relative to m_ref, probabilities are 2^score
+            unsigned pw[2][4];
+            float lsum = 0.f;
 #pragma unroll
-            for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);
-            bm = partner_max(bm);
-            const bool move = (kt == 0 && kb == 0) || bm > m_ref + kRescale;
-            if (__ballot(move)) {
-                const float m_new = move ? bm : m_ref;
-                const float corr = fast_exp2(m_ref - m_new);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    pw[t][u] = pack_bf(fast_exp2(sacc[kb][8 * t + 2 * u]), fast_exp2(sacc[kb][8 * t + 2 * u + 1]));
+                    lsum = dot2_bf(pw[t][u], kOnesBf16x2, lsum);
+                }
+            if (__ballot(first || !(lsum <= kSumLimit))) {
+                float bm = sacc[kb][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);
+                bm = partner_max(bm);  // block max relative to m_ref
+                const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm));
+                const float shift = m_new - m_ref;
+                if (!first) {
+                    const float corr = fast_exp2(-shift);
+                    l_run *= corr;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+                }
                 m_ref = m_new;
-                l_run *= corr;
+                // the second block's scores were taken against the old reference
+                if (kb == 0 && live[1]) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int r = 0; r < 16; ++r) sacc[1][r] -= shift;
+                }
+                negm_b = __builtin_bit_cast(bf16x8_t,
+                                            (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u});
+                lsum = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[db][r] *= corr;
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        pw[t][u] = pack_bf(fast_exp2(sacc[kb][8 * t + 2 * u] - shift),
+                                           fast_exp2(sacc[kb][8 * t + 2 * u + 1] - shift));
+                        lsum = dot2_bf(pw[t][u], kOnesBf16x2, lsum);
+                    }
             }
+            first = false;
+            l_run += lsum;
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
-                u32x4 vwr[NDB];
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) vwr[db] = *(const u32x4 *)(lt + vaddr + db * (32 * 128));
-                unsigned pw[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float p0 = fast_exp2(sacc[kb][8 * t + 2 * u] - m_ref);
-                    const float p1 = fast_exp2(sacc[kb][8 * t + 2 * u + 1] - m_ref);
-                    pw[u] = pack_bf(p0, p1);
-                    l_run = dot2_bf(pw[u], kOnesBf16x2, l_run);
-                }
-                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[t][0], pw[t][1], pw[t][2], pw[t][3]});
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, vwr[db]), pop, o[db], 0, 0, 0);
+                        __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(lt + vaddr + db * (32 * 128))), pop, o[db], 0, 0, 0);
             }
         }
 
@@ -504,6 +558,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         __syncthreads();
     }
 #undef ATF_TILE_LOAD
+#undef ATF_KOFF
 
     // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3)
     const float inv = 1.f / partner_sum(l_run);
