@@ -282,6 +282,79 @@ __device__ inline float bf16_ceil(float x) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0xffff0000u) : ((u + 0xffffu) & 0xffff0000u));
 }
 
+// Number of a lane's 16 key slots c_r = 8(r/4) + r%4 (r = 0..15) with c_r < x.
+__device__ inline int keys_below(int x) {
+    int n = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) n += min(max(x - 8 * g, 0), 4);
+    return n;
+}
+
+// Probabilities 2^s of one 32x32 score block (a lane's 16 keys) as 8 bf16
+// pairs, and their sum as the MFMA will see them (the rounded values).
+__device__ __attribute__((always_inline)) inline void block_probs(const f32x16_t &s, unsigned (&pw)[8],
+                                                                   float &lsum) {
+    constexpr unsigned kOnes = 0x3f803f80u;  // (1.0, 1.0) in bf16
+    lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        pw[u] = pack_bf(fast_exp2(s[2 * u]), fast_exp2(s[2 * u + 1]));
+        lsum = dot2_bf(pw[u], kOnes, lsum);
+    }
+}
+
+// O^T += V^T P^T for one 32-key block of the tile in LDS (lt): two K-steps
+// of 16 keys, NDB output blocks of 32 dims.
+template <int NDB>
+__device__ __attribute__((always_inline)) inline void block_pv(f32x16_t (&o)[NDB], const unsigned char *lt,
+                                                                unsigned vbase_lane, unsigned vz, int kb,
+                                                                const unsigned (&pw)[8]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[4 * t], pw[4 * t + 1], pw[4 * t + 2], pw[4 * t + 3]});
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(lt + vaddr + db * (32 * 128))), pop, o[db], 0, 0, 0);
+    }
+}
+
+// Second block's score chain and the first block's probabilities, written as
+// one straight-line sequence so the exponentials issue between the MFMAs.
+template <int NSTEP, int S0>
+__device__ __attribute__((always_inline)) inline f32x16_t qk_chain_probs(
+    const unsigned char *lds, unsigned kbase, unsigned ky, const bf16x8_t *qf, int zero_below, bf16x8_t ones_a,
+    bf16x8_t negm_b, const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
+    const f32x16_t acc = qk_chain<NSTEP, S0>(lds, kbase, ky, qf, zero_below, ones_a, negm_b);
+    block_probs(sp, pw, lsum);
+    return acc;
+}
+
+template <int NSTEP>
+__device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
+                                         const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b,
+                                         const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
+#define ATF_CHAIN(s0_) qk_chain_probs<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b, sp, pw, lsum)
+    switch (s_first) {
+        case 0: return ATF_CHAIN(0);
+        case 1: return ATF_CHAIN(1);
+        case 2: return ATF_CHAIN(2);
+        case 3: return ATF_CHAIN(3);
+        default: break;
+    }
+    if constexpr (NSTEP > 4) {
+        switch (s_first) {
+            case 4: return ATF_CHAIN(4);
+            case 5: return ATF_CHAIN(5);
+            case 6: return ATF_CHAIN(6);
+            default: return ATF_CHAIN((NSTEP > 4 ? 7 : 3));
+        }
+    }
+    return ATF_CHAIN(NSTEP - 1);
+#undef ATF_CHAIN
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     constexpr int P = D / 2;
@@ -376,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
-        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * (NLD * 1024);            \
+        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * (NLD * 1024);          \
         _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
             lds_dma16_buf(kr_, ATF_KOFF(n, c_min_), lk_ + n * 1024);                       \
             lds_dma16_buf(vr_, v_goff[n], lk_ + KT_BYTES + n * 1024);                      \
@@ -402,7 +475,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     // for every key row; B: -m_ref of the lane's query column), zeros elsewhere
     const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, (u32x4){half ? 0u : 0x3f80u, 0u, 0u, 0u});
     bf16x8_t negm_b = __builtin_bit_cast(bf16x8_t, (u32x4){0u, 0u, 0u, 0u});
-    unsigned long long skipped = 0;
+    // dropped-term count: per lane where it differs between lanes, uniform
+    // (whole-block) contributions in skipped_u
+    unsigned long long skipped = 0, skipped_u = 0;
+    const unsigned n_valid = (unsigned)__builtin_popcountll(__ballot(q_valid));
     const f32x16_t zero16 = {};
     const int koff0 = 4 * half;
     // per-lane LDS byte offsets (swizzle folded in)
@@ -422,137 +498,120 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * kKeyTile;
 
-        // ---- scores of both 32-key blocks: main chain, then that block's
-        // boundary pairs; the second block's MFMAs overlap the first block's softmax
+        // Per tile: chain 0 | chain 1 + probabilities 0 | P.V 0 + probabilities 1
+        // | P.V 1, so every MFMA run has independent VALU work beside it.
+        // Boundary pairs, diagonal masks and reference moves sit between the
+        // runs (rare branches).
         f32x16_t sacc[2];
-        bool live[2];
+        unsigned pw[2][8];
+        float lsum[2];
+        const bool live0 = j0 <= i0 + 31, live1 = j0 + 32 <= i0 + 31;
+        int p_lo[2], p_full[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jb = j0 + 32 * kb;
-            live[kb] = jb <= i0 + 31;
-            if (!live[kb]) continue;  // (a dead block's sacc is never read)
-            const int dmax = i0 + 31 - jb;
-            const int dmin = max(0, i0 - (jb + 31));
-            const int p_lo = __builtin_popcountll(__ballot(w_lane < dmin));
-            const int p_full = __builtin_popcountll(__ballot(w_lane < dmax));
-            const int s_first = p_full >> 3;
-            const unsigned kbase = kbase_lane + 32u * kb * (CH * 16);
-            sacc[kb] = qk_main<NSTEP>(s_first, lt, kbase, ky, qf, p_full - 8 * s_first - koff0, ones_a, negm_b);
-            const bool diag = jb + 31 > i0;  // some key may follow some query
-
-            // dropped terms of pairs below p_lo: every causal element of the block
-            if (q_valid && p_lo > 0) {
-                int ncausal = 16;
-                if (diag) {
-                    ncausal = 0;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        ncausal += (jb + 8 * (r >> 2) + koff0 + (r & 3) <= my_q) ? 1 : 0;
-                }
-                skipped += (unsigned long long)p_lo * (unsigned)ncausal;
-            }
-
-            // boundary pairs: one rank-2 MFMA each (key operand holds only pair
-            // p), added where the element's distance is inside W_p
-            if (p_lo < p_full) {
-#pragma unroll
-                for (int s = 0; s < NSTEP; ++s) {
-                    const int pa = max(p_lo, 8 * s), pe = min(p_full, 8 * s + 8);
-                    if (pa < pe) {
-                        const u32x4 kraw = *(const u32x4 *)(lt + kbase + ((32u * s) ^ ky));
-                        const int pb = 8 * s + koff0;
-                        for (int p = pa; p < pe; ++p) {
-                            u32x4 kw;
-                            kw.x = (pb + 0 == p) ? kraw.x : 0u;
-                            kw.y = (pb + 1 == p) ? kraw.y : 0u;
-                            kw.z = (pb + 2 == p) ? kraw.z : 0u;
-                            kw.w = (pb + 3 == p) ? kraw.w : 0u;
-                            const f32x16_t tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);
-                            const int Wp = __builtin_amdgcn_readlane(w_lane, p);
-                            int ndrop = 0;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int delta = my_q - (jb + 8 * (r >> 2) + koff0 + (r & 3));
-                                const bool keep = delta <= Wp;
-                                sacc[kb][r] += keep ? tp[r] : 0.f;
-                                ndrop += (!keep && delta >= 0) ? 1 : 0;
-                            }
-                            if (q_valid) skipped += (unsigned)ndrop;
-                        }
-                    }
-                }
-            }
+            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < max(0, i0 - (jb + 31))));
+            p_full[kb] = __builtin_popcountll(__ballot(w_lane < i0 + 31 - jb));
         }
 
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (!live[kb]) continue;
-            const int jb = j0 + 32 * kb;
-            const bool diag = jb + 31 > i0;
+        // boundary pairs (one rank-2 MFMA each, added where the distance is
+        // inside W_p), dropped-term count and causal mask of block kb
+#define ATF_BLOCK_EDGES(kb)                                                                       \
+        {                                                                                         \
+            const int jb = j0 + 32 * (kb);                                                        \
+            const bool diag = jb + 31 > i0;                                                       \
+            const unsigned kbase = kbase_lane + 32u * (kb) * (CH * 16);                           \
+            if (p_lo[kb] > 0) {                                                                   \
+                if (!diag) {                                                                      \
+                    skipped_u += (unsigned long long)p_lo[kb] * 16u * n_valid;                    \
+                } else if (q_valid) {                                                             \
+                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(my_q - koff0 - jb + 1); \
+                }                                                                                 \
+            }                                                                                     \
+            if (p_lo[kb] < p_full[kb]) {                                                          \
+                _Pragma("unroll") for (int s = 0; s < NSTEP; ++s) {                               \
+                    const int pa = max(p_lo[kb], 8 * s), pe = min(p_full[kb], 8 * s + 8);         \
+                    if (pa < pe) {                                                                \
+                        const u32x4 kraw = *(const u32x4 *)(lt + kbase + ((32u * s) ^ ky));       \
+                        const int pb = 8 * s + koff0;                                             \
+                        for (int p = pa; p < pe; ++p) {                                           \
+                            u32x4 kw;                                                             \
+                            kw.x = (pb + 0 == p) ? kraw.x : 0u;                                   \
+                            kw.y = (pb + 1 == p) ? kraw.y : 0u;                                   \
+                            kw.z = (pb + 2 == p) ? kraw.z : 0u;                                   \
+                            kw.w = (pb + 3 == p) ? kraw.w : 0u;                                   \
+                            const f32x16_t tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(          \
+                                __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);        \
+                            /* element r holds key jb + koff0 + c_r, c_r = 8(r/4) + r%4, at    \
+                               distance dq - c_r; it keeps pair p iff c_r >= dq - W_p */          \
+                            const int dq = my_q - koff0 - jb;                                     \
+                            const int lim = dq - __builtin_amdgcn_readlane(w_lane, p);            \
+                            _Pragma("unroll") for (int r = 0; r < 16; ++r)                        \
+                                sacc[kb][r] += (8 * (r >> 2) + (r & 3) >= lim) ? tp[r] : 0.f;     \
+                            if (q_valid) skipped += (unsigned)keys_below(min(lim, dq + 1));       \
+                        }                                                                         \
+                    }                                                                             \
+                }                                                                                 \
+            }                                                                                     \
+            if (diag) {                                                                           \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r)                                    \
+                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[kb][r] = -INFINITY;      \
+            }                                                                                     \
+        }
 
-            if (diag) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[kb][r] = -INFINITY;
-            }
+        // Move the reference when the block's probabilities overflow kSumLimit
+        // (or at the first block): block max becomes the reference, O and l are
+        // rescaled, the block's probabilities are redone; a later block of the
+        // same tile, scored against the old reference, is shifted too.
+#define ATF_BLOCK_RESCALE(kb, later_live)                                                         \
+        if (__ballot(first || !(lsum[kb] <= kSumLimit))) {                                        \
+            float bm = sacc[kb][0];                                                               \
+            _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);           \
+            bm = partner_max(bm);                                                                 \
+            const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm)); \
+            const float shift = m_new - m_ref;                                                    \
+            if (!first) {                                                                         \
+                const float corr = fast_exp2(-shift);                                             \
+                l_run *= corr;                                                                    \
+                _Pragma("unroll") for (int db = 0; db < NDB; ++db)                                \
+                    _Pragma("unroll") for (int r = 0; r < 16; ++r) o[db][r] *= corr;              \
+            }                                                                                     \
+            m_ref = m_new;                                                                        \
+            if (later_live) {                                                                     \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[1][r] -= shift;               \
+            }                                                                                     \
+            negm_b = __builtin_bit_cast(bf16x8_t,                                                 \
+                                        (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u}); \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;                  \
+            block_probs(sacc[kb], pw[kb], lsum[kb]);                                              \
+        }                                                                                         \
+        first = false;                                                                            \
+        l_run += lsum[kb];
 
-            // ---- online softmax for this block (lane and lane^32 share a query);
-            // scores are in log2 units relative to m_ref, probabilities are 2^score
-            unsigned pw[2][4];
-            float lsum = 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    pw[t][u] = pack_bf(fast_exp2(sacc[kb][8 * t + 2 * u]), fast_exp2(sacc[kb][8 * t + 2 * u + 1]));
-                    lsum = dot2_bf(pw[t][u], kOnesBf16x2, lsum);
-                }
-            if (__ballot(first || !(lsum <= kSumLimit))) {
-                float bm = sacc[kb][0];
-#pragma unroll
-                for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);
-                bm = partner_max(bm);  // block max relative to m_ref
-                const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm));
-                const float shift = m_new - m_ref;
-                if (!first) {
-                    const float corr = fast_exp2(-shift);
-                    l_run *= corr;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[db][r] *= corr;
-                }
-                m_ref = m_new;
-                // the second block's scores were taken against the old reference
-                if (kb == 0 && live[1]) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[1][r] -= shift;
-                }
-                negm_b = __builtin_bit_cast(bf16x8_t,
-                                            (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u});
-                lsum = 0.f;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        pw[t][u] = pack_bf(fast_exp2(sacc[kb][8 * t + 2 * u] - shift),
-                                           fast_exp2(sacc[kb][8 * t + 2 * u + 1] - shift));
-                        lsum = dot2_bf(pw[t][u], kOnesBf16x2, lsum);
-                    }
+        if (live0) {
+            const int sf0 = p_full[0] >> 3;
+            sacc[0] = qk_main<NSTEP>(sf0, lt, kbase_lane, ky, qf, p_full[0] - 8 * sf0 - koff0, ones_a, negm_b);
+            ATF_BLOCK_EDGES(0)
+            if (live1) {
+                const int sf1 = p_full[1] >> 3;
+                sacc[1] = qk_main_probs<NSTEP>(sf1, lt, kbase_lane + 32u * (CH * 16), ky, qf,
+                                               p_full[1] - 8 * sf1 - koff0, ones_a, negm_b, sacc[0], pw[0], lsum[0]);
+            } else {
+                block_probs(sacc[0], pw[0], lsum[0]);
             }
-            first = false;
-            l_run += lsum;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const unsigned vaddr = vbase_lane + ((32u * (2 * kb + t)) ^ vz);
-                const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[t][0], pw[t][1], pw[t][2], pw[t][3]});
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8_t, *(const u32x4 *)(lt + vaddr + db * (32 * 128))), pop, o[db], 0, 0, 0);
+            ATF_BLOCK_RESCALE(0, live1)
+            if (live1) {
+                ATF_BLOCK_EDGES(1)
+                block_pv<NDB>(o, lt, vbase_lane, vz, 0, pw[0]);
+                block_probs(sacc[1], pw[1], lsum[1]);
+                ATF_BLOCK_RESCALE(1, false)
+                block_pv<NDB>(o, lt, vbase_lane, vz, 1, pw[1]);
+            } else {
+                block_pv<NDB>(o, lt, vbase_lane, vz, 0, pw[0]);
             }
         }
+#undef ATF_BLOCK_EDGES
+#undef ATF_BLOCK_RESCALE
 
         __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile
         __syncthreads();
@@ -574,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                 *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
             }
     }
-    skipped = wave_sum_u64(skipped);
+    skipped = wave_sum_u64(skipped) + skipped_u;
     if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
 }
 
