@@ -127,6 +127,26 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
                               atf_dtype dtype, void *workspace, size_t workspace_bytes,
                               uint64_t *skipped_out, atf_stream_t stream);
 
+/*
+ * Chunked prefill: Sq new query tokens after a prefix of Sk - Sq cached
+ * tokens, all attending causally to the Sk keys (prefix + chunk).
+ *   q, out [B][Hq][Sq][d];  k, v [B][Hkv][Sk][d] (pre-RoPE, prefix first).
+ * Key j sits at pos0 + j; query i at pos0 + Sk - Sq + i, so query i sees keys
+ * 0 .. Sk - Sq + i and the windows apply to that distance exactly as in
+ * atf_prefill (Sq == Sk is atf_prefill).  Source page "ATFlash: ..."
+ * (sudo-ai.de), section "Die Zahlen - und ihre Grenze": the method drops into
+ * the prefill path unchanged, and a prefill continued over a cached prefix is
+ * that path with a query offset.  Needs 1 <= Sq <= Sk and
+ * atf_prefill_workspace_bytes(B, Hkv, Sk, d, dtype) bytes of workspace (the
+ * rotated keys of all Sk tokens).  Errors: Sq < 1 or Sq > Sk is
+ * ATF_ERR_INVALID_ARG; otherwise as atf_prefill with S = Sk.
+ */
+atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *out,
+                             int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d,
+                             double rope_base, double alpha, int32_t causal, int64_t pos0,
+                             atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                             uint64_t *skipped_out, atf_stream_t stream);
+
 /* ------------------------------------------------------------------- decode */
 
 /* Bytes of workspace atf_decode needs (per-split partial results + counter). */

@@ -25,7 +25,7 @@ W_INF = np.iinfo(np.int64).max
 EXPORTED = (
     "atf_status_string", "atf_version", "atf_window_table", "atf_skipped_pair_products",
     "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
-    "atf_prefill_attend", "atf_decode_workspace_bytes", "atf_decode",
+    "atf_prefill_attend", "atf_prefill_chunk", "atf_decode_workspace_bytes", "atf_decode",
 )
 
 
@@ -68,6 +68,9 @@ def _lib():
     lib.atf_prefill_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
                                        ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill_attend.restype = ctypes.c_int
+    lib.atf_prefill_chunk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, f64, f64, i32, i64,
+                                      ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_prefill_chunk.restype = ctypes.c_int
     lib.atf_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
     lib.atf_decode_workspace_bytes.restype = sz
     lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
@@ -201,6 +204,27 @@ def atf_prefill_attend(q, k, v, out, *, rope_base: float, alpha: float, causal: 
                                      _stream(q.device)),
            "atf_prefill_attend")
     return int(skipped.value) if return_skipped else None
+
+
+def atf_prefill_chunk(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
+                      ws=None, return_skipped: bool = False):
+    """Chunked prefill: q [B,Hq,Sq,d] are the last Sq of the Sk tokens whose
+    keys/values k, v [B,Hkv,Sk,d] hold (pre-RoPE); query i sits at pos0+Sk-Sq+i."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    nbytes = atf_prefill_workspace_bytes(B, Hkv, Sk, d, code)
+    if ws is None:
+        ws = workspace(nbytes, q.device, "prefill")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_prefill_chunk(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
+                                    B, Hq, Hkv, Sq, Sk, d, float(rope_base), float(alpha), int(causal),
+                                    int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                    ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_prefill_chunk")
+    return (out, int(skipped.value)) if return_skipped else out
 
 
 def atf_decode(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,

@@ -167,6 +167,54 @@ atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) 
     return ATF_OK;
 }
 
+// Attention over keys already prepared in the workspace: Sq query rows that
+// sit at key indices Sk - Sq .. Sk - 1 (positions pos0 + Sk - Sq + i), Sk keys
+// at positions pos0 + j.  Shapes are checked by the caller.
+atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
+                       int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, double rope_base, double alpha,
+                       int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                       uint64_t *skipped_out, hipStream_t s) {
+    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    AttnArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.out = out;
+    a.counter = (unsigned long long *)workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.Sq = (int)Sq;
+    a.Sk = (int)Sk;
+    a.Sk_pad = (int)padded_keys(Sk);
+    a.q_pos0 = pos0 + (Sk - Sq);
+    a.k_pos0 = pos0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    hipError_t e;
+    if (dtype == ATF_F32) {
+        // the fp32 kernel rotates raw keys itself: `krot` carries k, `vt` carries v
+        a.krot = k;
+        a.vt = v;
+        a.Sk_pad = (int)Sk;
+        e = launch_attend_f32(a, d, s);
+    } else {
+        char *ws = (char *)workspace + kHeaderBytes;
+        const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
+        a.krot = ws;
+        a.vt = ws + per;
+        a.n_qtiles = (int)((Sq + kQueryTile - 1) / kQueryTile);
+        a.n_groups = a.n_qtiles * B * Hkv;
+        e = launch_prefill_bf16(a, d, s);
+    }
+    if (e != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(a.counter, skipped_out, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,46 +299,8 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
                               size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
-    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
-    if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
-    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
-        return ATF_ERR_WORKSPACE;
-    AttnArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.q = q;
-    a.out = out;
-    a.counter = (unsigned long long *)workspace;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.group = Hq / Hkv;
-    a.Sq = (int)S;
-    a.Sk = (int)S;
-    a.Sk_pad = (int)padded_keys(S);
-    a.q_pos0 = pos0;
-    a.k_pos0 = pos0;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-    window_table_i32(d, rope_base, alpha, a.W);
-    theta_table(d, rope_base, a.theta);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    if (dtype == ATF_F32) {
-        // the fp32 kernel rotates raw keys itself: `krot` carries k, `vt` carries v
-        a.krot = k;
-        a.vt = v;
-        a.Sk_pad = (int)S;
-        e = launch_attend_f32(a, d, s);
-    } else {
-        char *ws = (char *)workspace + kHeaderBytes;
-        const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
-        a.krot = ws;
-        a.vt = ws + per;
-        a.n_qtiles = (int)((S + kQueryTile - 1) / kQueryTile);
-        a.n_groups = a.n_qtiles * B * Hkv;
-        e = launch_prefill_bf16(a, d, s);
-    }
-    if (e != hipSuccess) return ATF_ERR_HIP;
-    return read_counter(a.counter, skipped_out, s);
+    return attend_impl(q, k, v, out, B, Hq, Hkv, S, S, d, rope_base, alpha, pos0, dtype, workspace,
+                       workspace_bytes, skipped_out, stream);
 }
 
 atf_status atf_prefill(const void *q, const void *k, const void *v, void *out, int32_t B,
@@ -308,6 +318,23 @@ atf_status atf_prefill(const void *q, const void *k, const void *v, void *out, i
     if (st != ATF_OK) return st;
     return atf_prefill_attend(q, k, v, out, B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype,
                               workspace, workspace_bytes, skipped_out, stream);
+}
+
+atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *out, int32_t B,
+                             int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, double rope_base,
+                             double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                             size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+    if (Sq < 1 || Sq > Sk) return ATF_ERR_INVALID_ARG;
+    atf_status st = check_shape(B, Hq, Hkv, Sk, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    st = atf_prefill_prepare_kv(k, v, B, Hkv, Sk, d, rope_base, pos0, dtype, workspace, workspace_bytes,
+                                stream);
+    if (st != ATF_OK) return st;
+    return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_base, alpha, pos0, dtype, workspace,
+                       workspace_bytes, skipped_out, (hipStream_t)stream);
 }
 
 size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {

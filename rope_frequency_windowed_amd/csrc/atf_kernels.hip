@@ -381,9 +381,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, half = lane >> 5;
-    const int i0 = qt * kQueryTile + wave * 32;
+    const int i0 = qt * kQueryTile + wave * 32;  // first query row of this wave
     const int my_q = i0 + qi;
     const bool q_valid = my_q < a.Sq;
+    // Causal tests and distances run in key-index units: query row i sits at
+    // key index i + qoff (qoff = Sk - Sq > 0 when a prefix of cached keys
+    // precedes the query chunk).
+    const int qoff = (int)(a.q_pos0 - a.k_pos0);
+    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * kQueryTile + qoff;
     const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
 
     // ---- this lane's rotated, pre-scaled query in B-operand order: step s
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
 
     const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
-    const int last_key = min(a.Sk - 1, qt * kQueryTile + kQueryTile - 1);
+    const int last_key = min(a.Sk - 1, q0k + kQueryTile - 1);
     const int n_kt = last_key / kKeyTile + 1;
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
@@ -445,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
 #define ATF_TILE_LOAD(kt_, buf_)                                                           \
     {                                                                                      \
         const int j0_ = (kt_) * kKeyTile;                                                  \
-        const int dmin_wg_ = max(0, qt * kQueryTile - (j0_ + kKeyTile - 1));               \
+        const int dmin_wg_ = max(0, q0k - (j0_ + kKeyTile - 1));                          \
         const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
@@ -505,13 +510,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         f32x16_t sacc[2];
         unsigned pw[2][8];
         float lsum[2];
-        const bool live0 = j0 <= i0 + 31, live1 = j0 + 32 <= i0 + 31;
+        const bool live0 = j0 <= i0k + 31, live1 = j0 + 32 <= i0k + 31;
         int p_lo[2], p_full[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jb = j0 + 32 * kb;
-            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < max(0, i0 - (jb + 31))));
-            p_full[kb] = __builtin_popcountll(__ballot(w_lane < i0 + 31 - jb));
+            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < max(0, i0k - (jb + 31))));
+            p_full[kb] = __builtin_popcountll(__ballot(w_lane < i0k + 31 - jb));
         }
 
         // boundary pairs (one rank-2 MFMA each, added where the distance is
@@ -519,13 +524,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
 #define ATF_BLOCK_EDGES(kb)                                                                       \
         {                                                                                         \
             const int jb = j0 + 32 * (kb);                                                        \
-            const bool diag = jb + 31 > i0;                                                       \
+            const bool diag = jb + 31 > i0k;                                                      \
             const unsigned kbase = kbase_lane + 32u * (kb) * (CH * 16);                           \
             if (p_lo[kb] > 0) {                                                                   \
                 if (!diag) {                                                                      \
                     skipped_u += (unsigned long long)p_lo[kb] * 16u * n_valid;                    \
                 } else if (q_valid) {                                                             \
-                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(my_q - koff0 - jb + 1); \
+                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(my_qk - koff0 - jb + 1); \
                 }                                                                                 \
             }                                                                                     \
             if (p_lo[kb] < p_full[kb]) {                                                          \
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                                 __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);        \
                             /* element r holds key jb + koff0 + c_r, c_r = 8(r/4) + r%4, at    \
                                distance dq - c_r; it keeps pair p iff c_r >= dq - W_p */          \
-                            const int dq = my_q - koff0 - jb;                                     \
+                            const int dq = my_qk - koff0 - jb;                                    \
                             const int lim = dq - __builtin_amdgcn_readlane(w_lane, p);            \
                             _Pragma("unroll") for (int r = 0; r < 16; ++r)                        \
                                 sacc[kb][r] += (8 * (r >> 2) + (r & 3) >= lim) ? tp[r] : 0.f;     \
@@ -555,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
             }                                                                                     \
             if (diag) {                                                                           \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r)                                    \
-                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_q) sacc[kb][r] = -INFINITY;      \
+                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_qk) sacc[kb][r] = -INFINITY;     \
             }                                                                                     \
         }
 

@@ -140,3 +140,25 @@ def test_python_binding_needs_gpu_tensors(lib):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         atf.atf_prefill(q, q, q, rope_base=1e4, alpha=1.0)
+
+
+def _call_chunk(lib, **kw):
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, Sq=64, Sk=128, d=128, base=1e6, alpha=1.0,
+                causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_prefill_chunk(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]),
+                                 ctypes.c_void_p(args["v"]), ctypes.c_void_p(args["out"]), args["B"],
+                                 args["Hq"], args["Hkv"], args["Sq"], args["Sk"], args["d"], args["base"],
+                                 args["alpha"], args["causal"], args["pos0"], args["dtype"],
+                                 ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [(dict((("Sk" if k == "S" else k), v) for k, v in kw.items()), e)
+                                       for kw, e in BAD])
+def test_chunk_rejects(lib, kw, expect):
+    assert _call_chunk(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw", [dict(Sq=0), dict(Sq=-1), dict(Sq=129, Sk=128), dict(Sq=2, Sk=1)])
+def test_chunk_rejects_bad_lengths(lib, kw):
+    assert _call_chunk(lib, **kw) == bnd.ATF_ERR_INVALID_ARG

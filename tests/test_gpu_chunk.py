@@ -1,0 +1,146 @@
+"""GPU parity of chunked prefill (queries after a cached prefix) against the
+fp64 oracle, through the C ABI (atf_prefill_chunk)."""
+import math
+
+import numpy as np
+import pytest
+
+from parity import check_bf16, check_f32, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    require_gpu()
+    import torch
+
+    import oracle
+    import rope_frequency_windowed_amd as atf
+    from rope_frequency_windowed_amd import inputs
+    oracle.build()
+    return torch, oracle, atf, inputs
+
+
+def chunk_closed_form(atf, Sq, Sk, d, base, alpha):
+    """Per-head dropped terms: F(Sk-1) - F(Sk-Sq-1), F(T) = sum_p n(n+1)/2 with
+    n = max(0, T - W_p) (pinned against the oracle's enumeration on the CPU)."""
+    W = atf.atf_window_table(d, base, alpha)
+
+    def F(T):
+        tot = 0
+        for w in W:
+            if int(w) == atf.W_INF:
+                continue
+            n = max(0, T - int(w))
+            tot += n * (n + 1) // 2
+        return tot
+    return F(Sk - 1) - F(Sk - Sq - 1)
+
+
+def run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, dtype, pos0=0, hf=None):
+    torch, oracle, atf, inputs = env
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, Sq, Sk, d, dtype=dtype, device=dev, high_freq_scale=hf)
+    out, skipped = atf.atf_prefill_chunk(q, k, v, rope_base=base, alpha=alpha, pos0=pos0, return_skipped=True)
+    torch.cuda.synchronize()
+    return q, k, v, out, skipped
+
+
+CHUNK_BF16 = [
+    # B, Hq, Hkv, Sq, Sk, d, base, alpha
+    (1, 4, 2, 100, 1000, 128, 1e6, 1.0),    # ragged chunk after a ragged prefix
+    (1, 7, 1, 1, 777, 128, 1e6, 1.0),       # one query (decode-like, self key included)
+    (2, 4, 4, 333, 333, 64, 1e4, 0.5),      # no prefix: plain prefill
+    (1, 28, 4, 257, 5000, 128, 1e6, 2.0),   # benchmark head layout
+    (1, 2, 1, 64, 4096, 128, 1e6, 1.0),     # one query tile, long prefix
+    (1, 3, 1, 300, 2000, 64, 100.0, 0.3),   # tiny windows: most pairs cut
+    (1, 2, 1, 513, 1024, 128, 1e6, math.inf),  # no window
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d,base,alpha", CHUNK_BF16)
+def test_chunk_bf16(env, B, Hq, Hkv, Sq, Sk, d, base, alpha):
+    torch, oracle, atf, _ = env
+    log("case: chunk bf16 %s" % ((B, Hq, Hkv, Sq, Sk, d, base, alpha),))
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
+    dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, dense, "chunk %s" % ((B, Hq, Hkv, Sq, Sk, d),))
+    assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
+
+
+def test_chunk_high_frequency_heavy(env):
+    torch, oracle, atf, _ = env
+    log("case: chunk bf16 high-frequency-heavy")
+    q, k, v, out, skipped = run_chunk(env, 1, 4, 1, 200, 1500, 128, 1e6, 0.5, torch.bfloat16, hf=1.5)
+    ref, ref_skipped = oracle.attention(q, k, v, base=1e6, alpha=0.5, q_pos0=1300, k_pos0=0)
+    dense, _ = oracle.attention(q, k, v, base=1e6, alpha=math.inf, q_pos0=1300, k_pos0=0)
+    assert np.abs(dense - ref).max() > 0.05
+    check_bf16(out.float().cpu().numpy(), ref, dense, "chunk hf", structured=True)
+    assert skipped == ref_skipped
+
+
+@pytest.mark.parametrize("pos0", [1 << 20, 1 << 24])
+def test_chunk_position_shift(env, pos0):
+    torch, oracle, atf, _ = env
+    log("case: chunk pos0=%d" % pos0)
+    q, k, v, out, skipped = run_chunk(env, 1, 2, 1, 150, 700, 128, 1e6, 1.0, torch.bfloat16, pos0=pos0)
+    ref, ref_skipped = oracle.attention(q, k, v, base=1e6, alpha=1.0, q_pos0=pos0 + 550, k_pos0=pos0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "chunk pos0=%d" % pos0)
+    assert skipped == ref_skipped
+
+
+def test_chunk_without_prefix_is_prefill(env):
+    """Sq == Sk: atf_prefill_chunk and atf_prefill agree bit for bit."""
+    torch, oracle, atf, inputs = env
+    q, k, v = inputs.make_qkv(1, 4, 2, 700, 700, 128, dtype=torch.bfloat16, device=torch.device("cuda:0"))
+    a = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=1.0)
+    b = atf.atf_prefill_chunk(q, k, v, rope_base=1e6, alpha=1.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_chunk_matches_tail_of_full_prefill(env):
+    """The chunk's rows agree with the last Sq rows of the full prefill over
+    the Sk tokens (same math, different tiling)."""
+    torch, oracle, atf, inputs = env
+    dev = torch.device("cuda:0")
+    Sq, Sk = 300, 1100
+    q, k, v = inputs.make_qkv(1, 4, 1, Sk, Sk, 128, dtype=torch.bfloat16, device=dev)
+    full = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=1.0)
+    part = atf.atf_prefill_chunk(q[:, :, Sk - Sq:].contiguous(), k, v, rope_base=1e6, alpha=1.0)
+    torch.cuda.synchronize()
+    check_bf16(part.float().cpu().numpy(), full[:, :, Sk - Sq:].float().cpu().numpy(), None, "tail")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d", [(1, 4, 2, 37, 300, 64), (2, 7, 1, 100, 1000, 128)])
+def test_chunk_fp32(env, B, Hq, Hkv, Sq, Sk, d):
+    torch, oracle, atf, _ = env
+    log("case: chunk fp32 %s" % ((B, Hq, Hkv, Sq, Sk, d),))
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, 1e6, 1.0, torch.float32)
+    ref, ref_skipped = oracle.attention(q, k, v, base=1e6, alpha=1.0, q_pos0=Sk - Sq, k_pos0=0)
+    check_f32(out.cpu().numpy(), ref, "chunk fp32")
+    assert skipped == ref_skipped
+
+
+def test_chunk_long_prefix_sampled(env):
+    """A 4096-token chunk after a 126976-token prefix (Sk = 131072), benchmark
+    heads, on sampled rows plus the exact dropped-term count."""
+    torch, oracle, atf, _ = env
+    from rope_frequency_windowed_amd.inputs import sample_rows
+    B, Hq, Hkv, Sq, Sk, d, base, alpha = 1, 28, 4, 4096, 131072, 128, 1e6, 1.0
+    log("case: chunk Sq=%d Sk=%d" % (Sq, Sk))
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    assert skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
+    rows = np.array([(0, h, int(i)) for h in range(0, Hq, 3) for i in sample_rows(Sq, 4, seed=h)],
+                    dtype=np.int64)
+    sel = torch.as_tensor(rows, device=q.device)
+    qrows = q[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    got = out[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    kk, vv = k.float().cpu().numpy(), v.float().cpu().numpy()
+    ref, _ = oracle.attention(qrows, kk, vv, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0,
+                              rows=rows, q_shape=(B, Hq, Sq, d))
+    dense, _ = oracle.attention(qrows, kk, vv, base=base, alpha=math.inf, q_pos0=Sk - Sq, k_pos0=0,
+                                rows=rows, q_shape=(B, Hq, Sq, d))
+    check_bf16(got, ref, dense, "chunk long prefix")

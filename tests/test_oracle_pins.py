@@ -311,3 +311,36 @@ def test_windows_change_the_output(orc):
     a, _ = orc.attention(q, k, v, base=100.0, alpha=0.5)
     b, _ = orc.attention(q, k, v, base=100.0, alpha=math.inf)
     assert np.max(np.abs(a - b)) > 0.05
+
+
+def _chunk_closed_form(Sq, Sk, W):
+    """Dropped (query, key, pair) terms of one head when Sq queries sit at key
+    indices Sk-Sq .. Sk-1: query at index t drops pair p for the t - W_p keys
+    farther than W_p, so the count is F(Sk-1) - F(Sk-Sq-1) with
+    F(T) = sum_p n(n+1)/2, n = max(0, T - W_p)."""
+    def F(T):
+        tot = 0
+        for w in W:
+            if w == np.iinfo(np.int64).max:
+                continue
+            n = max(0, T - int(w))
+            tot += n * (n + 1) // 2
+        return tot
+    return F(Sk - 1) - F(Sk - Sq - 1)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(1, 40), (7, 40), (40, 40), (13, 100)])
+def test_chunk_equals_last_rows_of_full_prefill(orc, Sq, Sk):
+    """A chunk of Sq queries after Sk-Sq cached tokens is the last Sq rows of
+    the full causal prefill over Sk tokens, and its dropped-term count has the
+    closed form above (brute-force enumeration by the oracle)."""
+    d, base, alpha = 16, 10.0, 1.0
+    q = rnd((1, 2, Sk, d), 11)
+    k = rnd((1, 1, Sk, d), 12)
+    v = rnd((1, 1, Sk, d), 13)
+    full, _ = orc.attention(q, k, v, base=base, alpha=alpha, q_pos0=5, k_pos0=5)
+    qc = np.ascontiguousarray(q[:, :, Sk - Sq:, :])
+    part, cnt = orc.attention(qc, k, v, base=base, alpha=alpha, q_pos0=5 + Sk - Sq, k_pos0=5)
+    np.testing.assert_allclose(part, full[:, :, Sk - Sq:, :], rtol=0, atol=1e-12)
+    W = orc.window_table(d, base, alpha)
+    assert cnt == 2 * _chunk_closed_form(Sq, Sk, W)
