@@ -166,6 +166,55 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out,
                       atf_dtype dtype, void *workspace, size_t workspace_bytes,
                       uint64_t *skipped_out, atf_stream_t stream);
 
+/* --------------------------------------------- decode over a windowed key cache */
+
+/*
+ * A key cache laid out so that decode reads only the key dims the windows
+ * keep.  Source page "ATFlash: ..." (sudo-ai.de), section "Was ATFlash anders
+ * macht": beyond its window a pair's query-key term is dropped, so a key at
+ * distance D contributes only pairs [p*(D), P) (p*(D) = #{p : W_p < D}).  In
+ * the [S][d] layout both 128-byte halves of a d=128 key row always hold kept
+ * pairs, and memory is read in whole lines; this layout makes the kept pairs
+ * of a block of keys one contiguous byte range.
+ *
+ * Layout (bf16, device memory owned by the caller): for each (b, kv head), cap
+ * keys (cap a multiple of 64) in 64-key blocks; block c holds P/4 planes of
+ * 1024 bytes; plane pg holds, for each of the 64 keys, 16 bytes: pairs
+ * 4pg .. 4pg+3 of the key ROTATED at its position, each as (x'_p, x'_{p+P}):
+ *   byte ((b*Hkv + h) * (cap/64) + j/64) * (P/4 * 1024) + pg * 1024 + (j%64) * 16.
+ */
+
+/* Bytes of a key cache of capacity cap keys (0 if cap is not a positive
+ * multiple of 64 below 2^31 or d is not 64 or 128). */
+size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d);
+
+/*
+ * Writes keys into the cache: k [B][Hkv][n][d] (pre-RoPE, bf16) are cache keys
+ * k_begin .. k_begin + n - 1, rotated at positions pos0 + k_begin + i (an
+ * append when k_begin is the current length).  Requires 0 <= k_begin,
+ * k_begin + n <= cap, cap % 64 == 0, 0 <= pos0, pos0 + cap + 1 < 2^31.
+ * dtype must be ATF_BF16 (ATF_F32 returns ATF_ERR_UNSUPPORTED).  Asynchronous
+ * on `stream`.
+ */
+atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n,
+                             int64_t k_begin, int64_t cap, int32_t d, double rope_base,
+                             int64_t pos0, atf_dtype dtype, atf_stream_t stream);
+
+/*
+ * atf_decode over that cache: query q [B][Hq][1][d] at position pos0 + S over
+ * cache keys 0 .. S-1 (S <= cap) of kcache and value rows 0 .. S-1 of
+ * v [B][Hkv][cap][d] (standard layout, row stride cap).  Same result,
+ * windows, workspace (atf_decode_workspace_bytes(B, Hq, Hkv, S, d)) and
+ * skipped count as atf_decode; bf16 only.  Errors: cap not a multiple of 64,
+ * S > cap or pos0 + cap + 1 >= 2^31 is ATF_ERR_INVALID_ARG; otherwise as
+ * atf_decode.
+ */
+atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, void *out,
+                             int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int64_t cap, int32_t d,
+                             double rope_base, double alpha, int32_t causal, int64_t pos0,
+                             atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                             uint64_t *skipped_out, atf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,7 @@ EXPORTED = (
     "atf_status_string", "atf_version", "atf_window_table", "atf_skipped_pair_products",
     "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
     "atf_prefill_attend", "atf_prefill_chunk", "atf_decode_workspace_bytes", "atf_decode",
+    "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
 )
 
 
@@ -76,6 +77,13 @@ def _lib():
     lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
                                ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode.restype = ctypes.c_int
+    lib.atf_decode_kcache_bytes.argtypes = [i32, i32, i64, i32]
+    lib.atf_decode_kcache_bytes.restype = sz
+    lib.atf_decode_pack_k.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, f64, i64, ctypes.c_int, vp]
+    lib.atf_decode_pack_k.restype = ctypes.c_int
+    lib.atf_decode_kcache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, f64, f64, i32, i64,
+                                      ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_decode_kcache.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -246,6 +254,40 @@ def atf_decode(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int
                              code, _dev(ws, "workspace"), ws.numel(),
                              ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode")
+    return (out, int(skipped.value)) if return_skipped else out
+
+
+def atf_decode_kcache_bytes(B: int, Hkv: int, cap: int, d: int) -> int:
+    return int(_lib().atf_decode_kcache_bytes(B, Hkv, cap, d))
+
+
+def atf_decode_pack_k(k, kcache, *, k_begin: int, cap: int, rope_base: float, pos0: int = 0):
+    """Write k [B,Hkv,n,d] (pre-RoPE, bf16) as cache keys k_begin.. of kcache."""
+    B, Hkv, n, d = k.shape
+    _check(_lib().atf_decode_pack_k(_dev(k, "k"), _dev(kcache, "kcache"), B, Hkv, n, int(k_begin), int(cap), d,
+                                    float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
+           "atf_decode_pack_k")
+
+
+def atf_decode_kcache(q, kcache, v, out=None, *, S: int, rope_base: float, alpha: float, causal: int = 1,
+                      pos0: int = 0, ws=None, return_skipped: bool = False):
+    """Decode over the windowed key cache: q [B,Hq,1,d] at pos0+S, v [B,Hkv,cap,d]."""
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence")
+    Hkv, cap = v.shape[1], v.shape[2]
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    nbytes = atf_decode_workspace_bytes(B, Hq, Hkv, S, d)
+    if ws is None:
+        ws = workspace(nbytes, q.device, "decode")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_decode_kcache(_dev(q, "q"), _dev(kcache, "kcache"), _dev(v, "v"), _dev(out, "out"),
+                                    B, Hq, Hkv, int(S), cap, d, float(rope_base), float(alpha), int(causal),
+                                    int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                    ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_decode_kcache")
     return (out, int(skipped.value)) if return_skipped else out
 
 

@@ -403,4 +403,75 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
     return read_counter(counter, skipped_out, s);
 }
 
+size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d) {
+    if (B < 1 || Hkv < 1 || cap < kKeyTile || cap % kKeyTile != 0 || cap >= (int64_t)INT32_MAX) return 0;
+    if (d != 64 && d != 128) return 0;
+    return (size_t)B * Hkv * (size_t)cap * d * 2;
+}
+
+atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
+                             int64_t cap, int32_t d, double rope_base, int64_t pos0, atf_dtype dtype,
+                             atf_stream_t stream) {
+    if (!k || !kcache || !aligned16(k) || !aligned16(kcache)) return ATF_ERR_INVALID_ARG;
+    if (B < 1 || Hkv < 1 || n < 1 || k_begin < 0) return ATF_ERR_INVALID_ARG;
+    if (cap < kKeyTile || cap % kKeyTile != 0 || k_begin + n > cap) return ATF_ERR_INVALID_ARG;
+    if (d < 2 || (d & 1)) return ATF_ERR_INVALID_ARG;
+    if (!std::isfinite(rope_base) || !(rope_base > 1.0)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
+    if (pos0 < 0 || pos0 + cap + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
+    KPackArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.kc = kcache;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.n = (int)n;
+    a.cap = (int)cap;
+    a.k_begin = k_begin;
+    a.pos0 = pos0;
+    theta_table(d, rope_base, a.theta);
+    return hip_status(launch_kpack_bf16(a, d, (hipStream_t)stream));
+}
+
+atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, void *out, int32_t B,
+                             int32_t Hq, int32_t Hkv, int64_t S, int64_t cap, int32_t d, double rope_base,
+                             double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                             size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+    atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (cap < kKeyTile || cap % kKeyTile != 0 || S > cap || pos0 + cap + 1 >= (int64_t)INT32_MAX)
+        return ATF_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
+    if (!aligned16(workspace) || workspace_bytes < decode_ws_bytes(B, Hq, Hkv, S, d)) return ATF_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = kcache;
+    a.v = v;
+    a.out = out;
+    a.counter = (unsigned long long *)workspace;
+    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.S = (int)S;
+    a.cap = (int)cap;
+    a.pos0 = pos0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    DecodePlan plan;
+    plan_decode(B, Hq, Hkv, S, d, a.W, plan);
+    a.nsplit = plan.nsplit;
+    a.n_slabs = plan.n_slabs;
+    std::memcpy(a.split_start, plan.starts, sizeof(int) * (size_t)(plan.nsplit + 1));
+    if (launch_decode_kcache_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(a.counter, skipped_out, s);
+}
+
 }  // extern "C"

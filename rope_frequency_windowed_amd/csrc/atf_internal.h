@@ -55,6 +55,7 @@ struct DecodeArgs {
     void *out;
     unsigned long long *counter;
     int B, Hq, Hkv, group, S, nsplit, n_slabs;
+    int cap;                          // key-cache layout: keys per (b, kv head) row of k and v
     long long pos0;
     float scale_log2;
     int W[kMaxPairs];
@@ -62,7 +63,19 @@ struct DecodeArgs {
     int split_start[kMaxSplits + 1];  // key index where each split begins (multiple of 64)
 };
 
+// Writes keys into the decode key-cache layout (rotated, 64-key blocks of
+// 4-pair planes).
+struct KPackArgs {
+    const void *k;                    // [B][Hkv][n][d] pre-RoPE keys
+    void *kc;                         // the key cache, capacity cap keys per (b, kv head)
+    int B, Hkv, n, cap;
+    long long k_begin, pos0;          // key k[.., i, :] is cache key k_begin + i at pos0 + k_begin + i
+    double theta[kMaxPairs];
+};
+
 hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s);
+hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s);
+hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s);
 hipError_t launch_prep_f32(const PrepArgs &a, int d, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s);

@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace atf {
 namespace {
 
@@ -224,6 +226,11 @@ __device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned byt
 // so advancing the base costs no vector instructions.
 __device__ inline void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, void *dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, 0, 0, 0);
+}
+
+// 16 bytes at buffer offset voff (zeros, without a memory access, past the end).
+__device__ inline u32x4 raw_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
 // One block's main score chain starting at K-step S0 (compile time).
@@ -1103,6 +1110,324 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
 }
 
+// ============================================================================
+// Key-cache writer: rotates each key at its position and stores it in the
+// plane layout described below (one thread per (key, 4-pair plane): 8 bytes
+// of each rotary half in, 16 bytes out).  grid (x, B*Hkv), block 256.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(256) void kpack_bf16_kernel(KPackArgs a) {
+    constexpr int P = D / 2, NPL = P / 4;
+    constexpr unsigned KPBLK = NPL * 1024;
+    const int bk = blockIdx.y;
+    const long long total = (long long)a.n * NPL;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const int i = (int)(e / NPL), pg = (int)(e % NPL);
+        const long long j = a.k_begin + i;
+        const unsigned short *src = (const unsigned short *)a.k + ((long long)bk * a.n + i) * D + 4 * pg;
+        const u32x2 lo = *(const u32x2 *)src;
+        const u32x2 hi = *(const u32x2 *)(src + P);
+        unsigned r[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
+            const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
+            const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
+            float c, sn;
+            rope_cos_sin(a.pos0 + j, a.theta[4 * pg + w], c, sn);
+            r[w] = pack_bf(x * c - y * sn, y * c + x * sn);
+        }
+        unsigned char *dst = (unsigned char *)a.kc +
+                             ((long long)bk * (a.cap / kKeyTile) + j / kKeyTile) * KPBLK + pg * 1024 + (j % kKeyTile) * 16;
+        *(u32x4 *)dst = (u32x4){r[0], r[1], r[2], r[3]};
+    }
+}
+
+// ============================================================================
+// Split-KV decode over a key cache laid out for the windows (bf16).  Keys are
+// stored rotated (at their own positions) in 64-key blocks of P/4 planes; plane
+// pg holds pairs 4pg .. 4pg+3 of the block's 64 keys, 16 bytes per key, word w
+// = (x'_p, y'_p) of pair p = 4pg + w:
+//     byte ((b*Hkv + h) * cap/64 + j/64) * (P/4 * 1024) + pg * 1024 + (j % 64) * 16.
+// A key at distance D keeps pairs [p*(D), P), so a block keeps a suffix of its
+// planes, one contiguous byte range: the planes below the nearest key's cut
+// are never read, and HBM traffic shrinks with distance (in the standard
+// [S][d] layout each rotary half of a key is one 128-byte line that always
+// holds kept pairs, so every line is read).  The plane's 16 bytes are the
+// score MFMA's key operand as they stand: no rotation work in the loop.
+// Values stay in the standard layout, row stride cap.  Same split, chunk,
+// softmax, P.V and merge scheme as decode_bf16_kernel.
+// grid (nsplit, B*Hkv*n_slabs), block 256.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
+    constexpr int P = D / 2;
+    constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
+    constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
+    constexpr int CK = 32;               // keys per wave chunk
+    constexpr int VROW = D * 2;          // bytes per value row
+    constexpr int CHV = VROW / 16;       // 16-byte chunks per value row
+    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128)
+    constexpr int VR = 1024 / VROW;      // value rows per 1 KB direct-load piece
+    constexpr int H = kDecodeHeads;
+    constexpr unsigned KPBLK = (P / 4) * 1024;  // bytes of one 64-key block of the key cache
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf[4][VBYTES];
+    __shared__ float wm[4][16], wl[4][16];
+
+    const int split = blockIdx.x;
+    const int slab = blockIdx.y % a.n_slabs;
+    const int bk = blockIdx.y / a.n_slabs;
+    const int b = bk / a.Hkv, hk = bk % a.Hkv;
+    const int h0 = hk * a.group + slab * H;
+    const int nh = min(H, a.group - slab * H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = lane & 15, q = lane >> 4;
+    const long long qpos = a.pos0 + a.S;
+
+    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
+
+    // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
+    // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
+    bf16x8_t qf[NSTEP];
+    {
+        const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + t) * D;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+            if (t < nh) {
+                const int pb = 16 * s + 4 * q;
+                const u32x2 lo = *(const u32x2 *)(qrow + pb);
+                const u32x2 hi = *(const u32x2 *)(qrow + P + pb);
+                unsigned r[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
+                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
+                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
+                    float c, sn;
+                    rope_cos_sin(qpos, a.theta[pb + u], c, sn);
+                    r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
+                }
+                w = (u32x4){r[0], r[1], r[2], r[3]};
+            }
+            qf[s] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+    __syncthreads();
+
+    const int ks = a.split_start[split];
+    const int ke = min(a.split_start[split + 1], a.S);
+    const unsigned char *kpb = (const unsigned char *)a.k + (long long)bk * (a.cap / kKeyTile) * KPBLK;
+    const unsigned char *vbase = (const unsigned char *)a.v + (long long)bk * a.cap * VROW;
+    unsigned char *vb = vbuf[wave];
+
+    // Value rows are staged with 16-byte chunks swizzled: row r, chunk c at
+    // byte r*VROW + ((c ^ vsw(r)) << 4), vsw(r) = 2 (r mod CHV/2), so the
+    // transposed reads of a 16-lane group (4 rows x 32 bytes) hit distinct
+    // banks.  The chunk is prefetched into registers one chunk ahead (lane l
+    // of 1 KB piece m holds LDS bytes 1024 m + 16 l: row VR m + l / CHV,
+    // physical chunk l % CHV) and written to LDS when its turn comes.
+    constexpr int NVP = VBYTES / 1024;  // pieces per chunk
+    const int vlr = lane / CHV;
+    auto vsw = [](int r) { return 2 * (r % (CHV / 2)); };
+    u32x4 vreg[NVP];
+#define DEC_LOAD_V(jc_)                                                                 \
+    {                                                                                 \
+        const int nrow_ = min(CK, ke - (jc_));  /* rows past the split repeat its last row */ \
+        _Pragma("unroll") for (int m = 0; m < NVP; ++m) {                             \
+            const int row_ = VR * m + vlr;                                            \
+            const int c_ = (lane % CHV) ^ vsw(row_);                                  \
+            const int grow_ = (jc_) + min(row_, nrow_ - 1);                           \
+            vreg[m] = *(const u32x4 *)(vbase + (long long)grow_ * VROW + c_ * 16);    \
+        }                                                                             \
+    }
+    // this lane's transposed-read byte address for output block db, key group hh
+    auto vtr_addr = [&](int db, int hh) {
+        const int row = 16 * hh + 4 * q + (t >> 2);
+        const int col = 32 * db + 8 * (t & 3);  // byte column
+        return (unsigned)(row * VROW + ((((col >> 4) ^ vsw(row)) << 4) | (col & 15)));
+    };
+
+    f32x4_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    constexpr float kRescale = 8.f;
+    constexpr unsigned kOnesBf16x2 = 0x3f803f80u;
+    float m_ref = 0.f, l_run = 0.f;
+    bool first = true;
+    unsigned long long skipped = 0;
+
+    // Per-chunk key bookkeeping.  Dropped pairs per key: the chunk's nearest
+    // key has the fewest (p_near, one ballot); farther keys add the few
+    // windows that fall inside the chunk's distance range.
+#define DEC_CHUNK_KEYS(jc_, smin_, ps0_, ps1_)                                          \
+    {                                                                                 \
+        const int d_near_ = a.S - min((jc_) + CK - 1, ke - 1);                        \
+        const int d_far_ = a.S - (jc_);                                               \
+        const int p_near_ = __builtin_popcountll(__ballot(w_lane < d_near_));         \
+        smin_ = p_near_ >> 4;                                                         \
+        pmin = p_near_ >> 2;                                                          \
+        ps0_ = p_near_;                                                               \
+        ps1_ = p_near_;                                                               \
+        for (int pp = p_near_; pp < P - 1; ++pp) {                                    \
+            const int wpp = __builtin_amdgcn_readlane(w_lane, pp);                    \
+            if (wpp >= d_far_) break;                                                 \
+            ps0_ += (wpp < a.S - ((jc_) + t)) ? 1 : 0;                                \
+            ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;                           \
+        }                                                                             \
+        if ((jc_) + t >= ke) ps0_ = P;                                                \
+        if ((jc_) + 16 + t >= ke) ps1_ = P;                                           \
+    }
+    // Key planes of the last two K-steps (the only ones far keys keep) are
+    // loaded one chunk ahead into registers; nearer steps load on use.  A lane
+    // whose plane (4 s + q) lies wholly below the chunk's nearest key's cut
+    // reads past the end of the block's buffer: zeros, and no memory traffic.
+    // Rows past the split repeat its last key.
+    constexpr int SPRE = (NSTEP >= 2) ? NSTEP - 2 : 0;
+#define DEC_KOFF(pg_, row_) (((pg_) >= pmin) ? (unsigned)((pg_) * 1024 + (row_) * 16) : KPBLK)
+#define DEC_LOAD_K(jc_)                                                                 \
+    {                                                                                 \
+        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kpb + (long long)((jc_) / kKeyTile) * KPBLK, KPBLK); \
+        _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
+            const int row_ = min((jc_) + 16 * g + t, ke - 1) % kKeyTile;               \
+            _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i)                  \
+                kreg[g][i] = raw_load16(kr_, DEC_KOFF(4 * (SPRE + i) + q, row_));     \
+        }                                                                             \
+    }
+
+    int j0 = ks + wave * CK;
+    int s_min = 0, ps0 = P, ps1 = P, pmin = 0;
+    u32x4 kreg[2][NSTEP - SPRE];
+    if (j0 < ke) {
+        DEC_LOAD_V(j0);
+        DEC_CHUNK_KEYS(j0, s_min, ps0, ps1);
+        DEC_LOAD_K(j0);
+    }
+    for (; j0 < ke; j0 += 4 * CK) {
+        const int jn = j0 + 4 * CK;
+        // this chunk's values to LDS (the previous chunk's transposed reads,
+        // earlier in this wave's LDS order, are done with the buffer), then
+        // the next chunk's values into the freed registers
+#pragma unroll
+        for (int m = 0; m < NVP; ++m) *(u32x4 *)(vb + m * 1024 + lane * 16) = vreg[m];
+        if (jn < ke) DEC_LOAD_V(jn);
+        const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kpb + (long long)(j0 / kKeyTile) * KPBLK, KPBLK);
+
+        f32x4_t sc[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int u = 16 * g + t;  // key offset in the chunk
+            const int ps = g ? ps1 : ps0;
+            if (q == 0 && ps < P) skipped += (unsigned long long)ps * (unsigned)nh;
+            const int row = min(j0 + u, ke - 1) % kKeyTile;
+            f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) {
+                if (s < s_min) continue;
+                const int pb = 16 * s + 4 * q;
+                const u32x4 kw = (s >= SPRE) ? kreg[g][s - SPRE] : raw_load16(kr, DEC_KOFF(4 * s + q, row));
+                // words are rotated pairs (x'_p, y'_p), p = pb + w; drop p < p*(key)
+                const u32x4 r = (u32x4){(pb + 0 < ps) ? 0u : kw.x, (pb + 1 < ps) ? 0u : kw.y,
+                                        (pb + 2 < ps) ? 0u : kw.z, (pb + 3 < ps) ? 0u : kw.w};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r), qf[s], acc, 0, 0, 0);
+            }
+            // rows of acc are keys 4q + (0..3) of the group; drop keys past the split
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (j0 + 16 * g + 4 * q + i >= ke) acc[i] = -INFINITY;
+            sc[g] = acc;
+        }
+
+        // next chunk's keys: bookkeeping and the prefetched key pieces
+        if (jn < ke) {
+            DEC_CHUNK_KEYS(jn, s_min, ps0, ps1);
+            DEC_LOAD_K(jn);
+        }
+
+        // online softmax per head slot t (log2 units, lazy reference)
+        float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        bm = quad_max(bm);
+        const bool move = first || bm > m_ref + kRescale;
+        first = false;
+        if (__ballot(move)) {
+            const float m_new = move ? bm : m_ref;
+            const float corr = fast_exp2(m_ref - m_new);
+            m_ref = m_new;
+            l_run *= corr;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= corr;
+        }
+        unsigned pw[4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            pw[2 * g] = pack_bf(fast_exp2(sc[g][0] - m_ref), fast_exp2(sc[g][1] - m_ref));
+            pw[2 * g + 1] = pack_bf(fast_exp2(sc[g][2] - m_ref), fast_exp2(sc[g][3] - m_ref));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
+        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+
+        // P.V on this chunk's values (written to LDS by this wave above)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const u32x2 v0 = lds_read_tr16(vb, vtr_addr(db, 0));
+            const u32x2 v1 = lds_read_tr16(vb, vtr_addr(db, 1));
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}), pop, o[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+#undef DEC_CHUNK_KEYS
+#undef DEC_LOAD_K
+#undef DEC_LOAD_V
+#undef DEC_KOFF
+
+    // ---- merge the 4 waves (reuses the value buffers) and write partials
+    l_run = quad_sum(l_run);
+    __syncthreads();
+    float *wo = (float *)&vbuf[0][0];  // [4][H][D]
+    if (t < nh) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wo[(wave * H + t) * D + 16 * db + 4 * q + i] = o[db][i];
+    }
+    if (q == 0) {
+        wm[wave][t] = first ? -INFINITY : m_ref;  // a wave without keys contributes nothing
+        wl[wave][t] = l_run;
+    }
+    __syncthreads();
+    for (int e = tid; e < nh * (D + 2); e += 256) {
+        const int hh = e / (D + 2), c = e % (D + 2);
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][hh]);
+        float val;
+        if (c == D) {
+            val = M;
+        } else {
+            val = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float f = (wm[w][hh] == -INFINITY) ? 0.f : fast_exp2(wm[w][hh] - M);
+                val += f * ((c < D) ? wo[(w * H + hh) * D + c] : wl[w][hh]);
+            }
+        }
+        a.part[((long long)(b * a.Hq + h0 + hh) * a.nsplit + split) * (D + 2) + c] = val;
+    }
+    skipped = wave_sum_u64(skipped);
+    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+}
+
+
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // grid B*Hq, block D.
 template <int D>
@@ -1160,6 +1485,27 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
     if (d == 128) decode_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else decode_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d == 128) decode_combine_kernel<128><<<a.B * a.Hq, 128, 0, s>>>(a);
+    else decode_combine_kernel<64><<<a.B * a.Hq, 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s) {
+    const long long total = (long long)a.n * (d / 8);
+    const unsigned gx = (unsigned)std::min<long long>((total + 255) / 256, 65535);
+    dim3 grid(gx, (unsigned)(a.B * a.Hkv));
+    if (d == 128) kpack_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    else kpack_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) {
+    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
+    if (d == 128) decode_kcache_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    else decode_kcache_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d == 128) decode_combine_kernel<128><<<a.B * a.Hq, 128, 0, s>>>(a);

@@ -162,3 +162,58 @@ def test_chunk_rejects(lib, kw, expect):
 @pytest.mark.parametrize("kw", [dict(Sq=0), dict(Sq=-1), dict(Sq=129, Sk=128), dict(Sq=2, Sk=1)])
 def test_chunk_rejects_bad_lengths(lib, kw):
     assert _call_chunk(lib, **kw) == bnd.ATF_ERR_INVALID_ARG
+
+
+def test_kcache_bytes(lib):
+    assert atf.atf_decode_kcache_bytes(8, 4, 262144, 128) == 8 * 4 * 262144 * 128 * 2
+    assert atf.atf_decode_kcache_bytes(1, 1, 64, 64) == 64 * 64 * 2
+    for bad in [(1, 1, 100, 128), (1, 1, 0, 128), (0, 1, 64, 128), (1, 1, 64, 96), (1, 1, 1 << 31, 128)]:
+        assert atf.atf_decode_kcache_bytes(*bad) == 0
+
+
+def _call_pack(lib, **kw):
+    args = dict(k=32, kc=4096, B=1, Hkv=2, n=10, k_begin=0, cap=128, d=128, base=1e6, pos0=0,
+                dtype=atf.ATF_BF16, stream=None)
+    args.update(kw)
+    return lib.atf_decode_pack_k(ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["kc"]), args["B"], args["Hkv"],
+                                 args["n"], args["k_begin"], args["cap"], args["d"], args["base"], args["pos0"],
+                                 args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=None), bnd.ATF_ERR_INVALID_ARG), (dict(kc=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(kc=4100), bnd.ATF_ERR_INVALID_ARG), (dict(n=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(k_begin=-1), bnd.ATF_ERR_INVALID_ARG), (dict(cap=100), bnd.ATF_ERR_INVALID_ARG),
+    (dict(k_begin=120, n=10), bnd.ATF_ERR_INVALID_ARG), (dict(d=63), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=96), bnd.ATF_ERR_UNSUPPORTED), (dict(base=1.0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(pos0=-1), bnd.ATF_ERR_INVALID_ARG), (dict(pos0=(1 << 31) - 100), bnd.ATF_ERR_INVALID_ARG),
+    (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=5), bnd.ATF_ERR_INVALID_ARG),
+])
+def test_pack_rejects(lib, kw, expect):
+    assert _call_pack(lib, **kw) == expect
+
+
+def _call_kcache(lib, **kw):
+    args = dict(q=16, kc=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, cap=128, d=128, base=1e6, alpha=1.0,
+                causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_decode_kcache(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["kc"]),
+                                 ctypes.c_void_p(args["v"]), ctypes.c_void_p(args["out"]), args["B"],
+                                 args["Hq"], args["Hkv"], args["S"], args["cap"], args["d"], args["base"],
+                                 args["alpha"], args["causal"], args["pos0"], args["dtype"],
+                                 ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [(dict(((k if k != "k" else "kc"), v) for k, v in kw.items()), e)
+                                       for kw, e in BAD if "S" not in kw])
+def test_kcache_decode_rejects(lib, kw, expect):
+    assert _call_kcache(lib, **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cap=100), bnd.ATF_ERR_INVALID_ARG), (dict(S=129), bnd.ATF_ERR_INVALID_ARG),
+    (dict(S=0), bnd.ATF_ERR_INVALID_ARG), (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(pos0=(1 << 31) - 130), bnd.ATF_ERR_INVALID_ARG),
+])
+def test_kcache_decode_rejects_layout(lib, kw, expect):
+    assert _call_kcache(lib, **kw) == expect
