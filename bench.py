@@ -3,16 +3,18 @@
 
 One step = one causal prefill of S=131072 tokens (B=1, Hq=28, Hkv=4, d=128,
 RoPE base 1e6, alpha=1, bf16 with fp32 accumulation) followed by one decode
-step (B=8 sequences, one query each after a 262144-key cache, same heads),
+step (B=8 sequences, one query each after a 262144-key cache, same heads)
+over the standard [S][d] cache and one over the windowed key-cache layout,
 inputs iid N(0,1) from fixed seeds, already resident in HBM.
 
 Printed: one JSON line.  `value` is prefill tokens/s; the `roofline` object
 is for the dominant kernel (the prefill attention kernel, MFMA-bound; the
 algorithmic flops count only the pair products the windows keep plus P.V);
-`decode` carries the decode step's algorithmic HBM rate against its roofline;
-`cpu_baseline` is the fp64 oracle timed on a bounded sample on the host.
+`decode` and `decode_kcache` carry the decode steps' algorithmic HBM rates
+against their roofline; `cpu_baseline` is the fp64 oracle timed on a bounded
+sample on the host.
 
-  python bench.py [--steps K] [--warmup W] [--only prefill|decode] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache] [--no-cpu]
   python bench.py --copy-probe      (plain copy kernel of known size, for the
                                      HBM-counter scale factor)
 """
@@ -35,6 +37,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
 KERNEL_SRC = os.path.join(ROOT, "rope_frequency_windowed_amd", "csrc", "atf_kernels.hip")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_counters.txt")
 DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kv262144_counters.txt")
+KCACHE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kcache_kv262144_counters.txt")
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
@@ -141,7 +144,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "kcache"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -163,6 +166,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
+    do_kcache = args.only in (None, "kcache")
 
     if do_prefill:
         P = PREFILL
@@ -183,6 +187,17 @@ def main():
         dout = torch.empty_like(dq)
         dws = torch.empty(atf.atf_decode_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
                           dtype=torch.uint8, device=dev)
+    if do_kcache:
+        D = DECODE
+        kq, kk, kv = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
+        kout = torch.empty_like(kq)
+        kws = torch.empty(atf.atf_decode_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
+                          dtype=torch.uint8, device=dev)
+        # the cache is filled once, as a serving cache would be (appends are per token)
+        kcache = torch.empty(atf.atf_decode_kcache_bytes(D["B"], D["Hkv"], D["S"], D["d"]),
+                             dtype=torch.uint8, device=dev)
+        atf.atf_decode_pack_k(kk, kcache, k_begin=0, cap=D["S"], rope_base=D["base"])
+        del kk
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -201,12 +216,19 @@ def main():
             atf.atf_decode(dq, dk, dv, dout, rope_base=D["base"], alpha=D["alpha"], ws=dws)
             if ev is not None:
                 ev[4].record(stream)
+        if do_kcache:
+            if ev is not None:
+                ev[5].record(stream)
+            atf.atf_decode_kcache(kq, kcache, kv, kout, S=DECODE["S"], rope_base=DECODE["base"],
+                                  alpha=DECODE["alpha"], ws=kws)
+            if ev is not None:
+                ev[6].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -246,6 +268,20 @@ def main():
         log("decode: %.3f ms, %.3g algorithmic bytes, %.0f GB/s (%.1f%% of HBM peak)"
             % (dec_ms, nbytes, gbs, 100 * gbs / HBM_PEAK_GBS))
         if not do_prefill:
+            res["value"], res["unit"] = gbs, "GB/s"
+    if do_kcache:
+        kc_ms = sum(e[5].elapsed_time(e[6]) for e in events) / args.steps
+        nbytes = decode_algorithmic_bytes(atf, **DECODE)
+        gbs = nbytes / (kc_ms * 1e-3) / 1e9
+        res["decode_kcache"] = {
+            "value": gbs, "unit": "GB/s", "ms": kc_ms, "tok_per_s": DECODE["B"] / (kc_ms * 1e-3),
+            "layout": "rotated keys in 64-key blocks of 4-pair planes (atf_decode_pack_k)",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                         "traffic": read_traffic(KCACHE_COUNTERS_FILE)}}
+        log("decode (key-cache layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
+            % (kc_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+        if not do_prefill and not do_decode:
             res["value"], res["unit"] = gbs, "GB/s"
     res["config"] = config
     if do_prefill and not args.no_cpu:
