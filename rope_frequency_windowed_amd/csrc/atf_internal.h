@@ -9,14 +9,23 @@ namespace atf {
 
 constexpr int kMaxPairs = 64;     // d <= 128
 constexpr int kKeyTile = 64;      // keys per prefill tile / decode chunk
-constexpr int kQueryTile = 128;   // queries per prefill workgroup (bf16)
+#ifndef ATF_PREFILL_WAVES
+#define ATF_PREFILL_WAVES 8
+#endif
+#ifndef ATF_PREFILL_KEYS
+#define ATF_PREFILL_KEYS 128
+#endif
+constexpr int kPrefillWaves = ATF_PREFILL_WAVES;       // waves per prefill workgroup (bf16)
+constexpr int kPrefillKeys = ATF_PREFILL_KEYS;         // keys per prefill LDS tile (bf16)
+constexpr int kQueryTile = 32 * kPrefillWaves;         // queries per prefill workgroup (bf16)
 constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
 constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
 constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves
 constexpr int kWindowInf = 0x7fffffff;
 
 // Padded key count: every tile is full, padding rows hold zeros.
-inline int64_t padded_keys(int64_t S) { return (S + kKeyTile - 1) / kKeyTile * kKeyTile; }
+// rotated-key / transposed-value rows kept per (b, kv head): whole prefill tiles
+inline int64_t padded_keys(int64_t S) { return (S + kPrefillKeys - 1) / kPrefillKeys * kPrefillKeys; }
 
 // Arguments of the key/value preparation pass.
 struct PrepArgs {

@@ -224,8 +224,8 @@ __device__ inline __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, unsigned byt
 
 // Same as lds_dma16, addressed as buffer base (SGPRs) + per-lane byte offset,
 // so advancing the base costs no vector instructions.
-__device__ inline void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, void *dst) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, 0, 0, 0);
+__device__ inline void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, int soff, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, soff, 0, 0);
 }
 
 // 16 bytes at buffer offset voff (zeros, without a memory access, past the end).
@@ -363,14 +363,18 @@ __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, 
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill_bf16_kernel(AttnArgs a) {
     constexpr int P = D / 2;
-    constexpr int NSTEP = D / 16;   // MFMA K-steps of 16 dims (8 pairs)
-    constexpr int CH = D / 8;       // 16-byte chunks per rotated-key row
-    constexpr int NDB = D / 32;     // 32-dim blocks of the output
-    constexpr int NLD = CH / 4;     // 1 KB direct loads per wave per tile (each of K', V^T)
-    constexpr unsigned KT_BYTES = kKeyTile * D * 2;
-    constexpr unsigned TILE_BYTES = 2 * KT_BYTES;  // K' then V^T
+    constexpr int NW = kPrefillWaves;  // waves per workgroup (two per SIMD)
+    constexpr int KT = kPrefillKeys;   // keys per LDS tile
+    constexpr int NB = KT / 32;        // 32-key score blocks per tile
+    constexpr int NSTEP = D / 16;      // MFMA K-steps of 16 dims (8 pairs)
+    constexpr int CH = D / 8;          // 16-byte chunks per rotated-key row
+    constexpr int NDB = D / 32;        // 32-dim blocks of the output
+    constexpr unsigned KT_BYTES = KT * D * 2;
+    constexpr unsigned TILE_BYTES = 2 * KT_BYTES;  // K' then V^T (KT/64 tiles of [D][64])
+    constexpr int NLD = KT_BYTES / 1024 / NW;      // 1 KB direct loads per wave per tile (each of K', V^T)
+    static_assert(NLD >= 1 && NB % 2 == 0, "tile shape");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
 
     // ---- work item: longest query tiles first; the group heads sharing one kv
@@ -432,39 +436,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const int last_key = min(a.Sk - 1, q0k + kQueryTile - 1);
-    const int n_kt = last_key / kKeyTile + 1;
+    const int n_kt = last_key / KT + 1;
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
     // wave's n-th 1 KB piece lands at LDS byte piece*1024 + 16 l (lane-linear),
     // so the lane fetches the global chunk that the swizzle puts there.  Key
     // chunks whose pairs no block of this workgroup can use are not fetched
     // (c_min: first 16-byte chunk any wave reads in this tile).
-    // per-lane byte offsets of this wave's direct-load pieces (loop invariant)
-    unsigned k_goff[NLD], v_goff[NLD];
-    int k_chunk[NLD];
-#pragma unroll
-    for (int n = 0; n < NLD; ++n) {
-        const int kbyte = (wave * NLD + n) * 1024 + lane * 16;
+    // Piece n of wave w is tile piece n*NW + w, so every piece of a lane has
+    // the same swizzle: one per-lane offset, plus n * NW KB in a scalar.
+    unsigned k_goff, v_goff;
+    int k_chunk;
+    {
+        const int kbyte = wave * 1024 + lane * 16;
         const int krow = kbyte / (CH * 16);
-        k_chunk[n] = ((kbyte / 16) % CH) ^ kswz<CH>(krow);
-        k_goff[n] = (unsigned)(krow * (CH * 16) + k_chunk[n] * 16);
+        k_chunk = ((kbyte / 16) % CH) ^ kswz<CH>(krow);
+        k_goff = (unsigned)(krow * (CH * 16) + k_chunk * 16);
         const int vrow = kbyte / 128;
-        v_goff[n] = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
+        v_goff = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
     }
+    static_assert((NW * 1024) % (CH * 16 * 16) == 0 && (NW * 1024) % (128 * 16) == 0,
+                  "a piece stride must keep the row swizzles");
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    // a key chunk below c_min is not fetched: its offset is past the buffer's end
-#define ATF_KOFF(n_, cmin_) ((k_chunk[n_] >= (cmin_)) ? k_goff[n_] : KT_BYTES)
 #define ATF_TILE_LOAD(kt_, buf_)                                                           \
     {                                                                                      \
-        const int j0_ = (kt_) * kKeyTile;                                                  \
-        const int dmin_wg_ = max(0, q0k - (j0_ + kKeyTile - 1));                          \
+        const int j0_ = (kt_) * KT;                                                        \
+        const int dmin_wg_ = max(0, q0k - (j0_ + KT - 1));                                 \
         const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
+        /* a key chunk below c_min is not fetched: its offset is past the buffer's end */ \
+        const unsigned koff_ = (k_chunk >= c_min_) ? k_goff : KT_BYTES;                    \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
-        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * (NLD * 1024);          \
+        unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * 1024;                    \
         _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
-            lds_dma16_buf(kr_, ATF_KOFF(n, c_min_), lk_ + n * 1024);                       \
-            lds_dma16_buf(vr_, v_goff[n], lk_ + KT_BYTES + n * 1024);                      \
+            lds_dma16_buf(kr_, koff_, n * NW * 1024, lk_ + n * NW * 1024);                 \
+            lds_dma16_buf(vr_, v_goff, n * NW * 1024, lk_ + KT_BYTES + n * NW * 1024);     \
         }                                                                                  \
     }
 
@@ -480,7 +486,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
     // then the block's exact max becomes the reference and the block is redone.
     // Probabilities therefore stay below kSumLimit and the O rescale is rare.
     constexpr float kSumLimit = 4096.f;
-    constexpr unsigned kOnesBf16x2 = 0x3f803f80u;  // (1.0, 1.0) in bf16
     float m_ref = 0.f, l_run = 0.f;
     bool first = true;
     // rank-1 operands of the reference: element k = 0 of lanes 0..31 (A: ones
@@ -508,27 +513,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         const int buf = kt & 1;
         if (kt + 1 < n_kt) ATF_TILE_LOAD(kt + 1, buf ^ 1);
         const unsigned char *lt = lds + buf * TILE_BYTES;
-        const int j0 = kt * kKeyTile;
+        const int j0 = kt * KT;
 
-        // Per tile: chain 0 | chain 1 + probabilities 0 | P.V 0 + probabilities 1
-        // | P.V 1, so every MFMA run has independent VALU work beside it.
-        // Boundary pairs, diagonal masks and reference moves sit between the
-        // runs (rare branches).
+        // Per pair of 32-key blocks: chain0 | chain1 + probs0 | PV0 + probs1 |
+        // PV1, so every MFMA run but the first and last has independent VALU
+        // work beside it.  Boundary pairs, diagonal masks and reference moves
+        // sit between the runs (rare branches).
         f32x16_t sacc[2];
         unsigned pw[2][8];
         float lsum[2];
-        const bool live0 = j0 <= i0k + 31, live1 = j0 + 32 <= i0k + 31;
-        int p_lo[2], p_full[2];
+        int p_lo[NB], p_full[NB];
+        bool live[NB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NB; ++kb) {
             const int jb = j0 + 32 * kb;
+            live[kb] = jb <= i0k + 31;
             p_lo[kb] = __builtin_popcountll(__ballot(w_lane < max(0, i0k - (jb + 31))));
             p_full[kb] = __builtin_popcountll(__ballot(w_lane < i0k + 31 - jb));
         }
 
         // boundary pairs (one rank-2 MFMA each, added where the distance is
-        // inside W_p), dropped-term count and causal mask of block kb
-#define ATF_BLOCK_EDGES(kb)                                                                       \
+        // inside W_p), dropped-term count and causal mask of block kb (slot sl)
+#define ATF_BLOCK_EDGES(kb, sl)                                                                   \
         {                                                                                         \
             const int jb = j0 + 32 * (kb);                                                        \
             const bool diag = jb + 31 > i0k;                                                      \
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                             const int dq = my_qk - koff0 - jb;                                    \
                             const int lim = dq - __builtin_amdgcn_readlane(w_lane, p);            \
                             _Pragma("unroll") for (int r = 0; r < 16; ++r)                        \
-                                sacc[kb][r] += (8 * (r >> 2) + (r & 3) >= lim) ? tp[r] : 0.f;     \
+                                sacc[sl][r] += (8 * (r >> 2) + (r & 3) >= lim) ? tp[r] : 0.f;     \
                             if (q_valid) skipped += (unsigned)keys_below(min(lim, dq + 1));       \
                         }                                                                         \
                     }                                                                             \
@@ -567,18 +573,18 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
             }                                                                                     \
             if (diag) {                                                                           \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r)                                    \
-                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_qk) sacc[kb][r] = -INFINITY;     \
+                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_qk) sacc[sl][r] = -INFINITY;     \
             }                                                                                     \
         }
 
-        // Move the reference when the block's probabilities overflow kSumLimit
+        // Move the reference when block kb's probabilities overflow kSumLimit
         // (or at the first block): block max becomes the reference, O and l are
-        // rescaled, the block's probabilities are redone; a later block of the
-        // same tile, scored against the old reference, is shifted too.
-#define ATF_BLOCK_RESCALE(kb, later_live)                                                         \
-        if (__ballot(first || !(lsum[kb] <= kSumLimit))) {                                        \
-            float bm = sacc[kb][0];                                                               \
-            _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[kb][r]);           \
+        // rescaled, the block's probabilities are redone; the next block, already
+        // scored against the old reference (when `later` holds), is shifted too.
+#define ATF_BLOCK_RESCALE(sl, later)                                                              \
+        if (__ballot(first || !(lsum[sl] <= kSumLimit))) {                                        \
+            float bm = sacc[sl][0];                                                               \
+            _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[sl][r]);           \
             bm = partner_max(bm);                                                                 \
             const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm)); \
             const float shift = m_new - m_ref;                                                    \
@@ -589,37 +595,43 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
                     _Pragma("unroll") for (int r = 0; r < 16; ++r) o[db][r] *= corr;              \
             }                                                                                     \
             m_ref = m_new;                                                                        \
-            if (later_live) {                                                                     \
-                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[1][r] -= shift;               \
+            if (later) {                                                                          \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[(sl) ^ 1][r] -= shift;        \
             }                                                                                     \
             negm_b = __builtin_bit_cast(bf16x8_t,                                                 \
                                         (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u}); \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;                  \
-            block_probs(sacc[kb], pw[kb], lsum[kb]);                                              \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[sl][r] -= shift;                  \
+            block_probs(sacc[sl], pw[sl], lsum[sl]);                                              \
         }                                                                                         \
         first = false;                                                                            \
-        l_run += lsum[kb];
+        l_run += lsum[sl];
 
-        if (live0) {
-            const int sf0 = p_full[0] >> 3;
-            sacc[0] = qk_main<NSTEP>(sf0, lt, kbase_lane, ky, qf, p_full[0] - 8 * sf0 - koff0, ones_a, negm_b);
-            ATF_BLOCK_EDGES(0)
+#pragma unroll
+        for (int kp = 0; kp < NB; kp += 2) {  // pairs of blocks: slot 0 = block kp, slot 1 = kp + 1
+            if (!live[kp]) break;
+            const unsigned char *lv = lt + (kp >> 1) * (D * 128);  // the pair's 64-key V^T tile
+            const int sf0 = p_full[kp] >> 3;
+            sacc[0] = qk_main<NSTEP>(sf0, lt, kbase_lane + 32u * kp * (CH * 16), ky, qf,
+                                     p_full[kp] - 8 * sf0 - koff0, ones_a, negm_b);
+            ATF_BLOCK_EDGES(kp, 0)
+            const bool live1 = live[kp + 1];
             if (live1) {
-                const int sf1 = p_full[1] >> 3;
-                sacc[1] = qk_main_probs<NSTEP>(sf1, lt, kbase_lane + 32u * (CH * 16), ky, qf,
-                                               p_full[1] - 8 * sf1 - koff0, ones_a, negm_b, sacc[0], pw[0], lsum[0]);
+                const int sf1 = p_full[kp + 1] >> 3;
+                sacc[1] = qk_main_probs<NSTEP>(sf1, lt, kbase_lane + 32u * (kp + 1) * (CH * 16), ky, qf,
+                                               p_full[kp + 1] - 8 * sf1 - koff0, ones_a, negm_b, sacc[0], pw[0],
+                                               lsum[0]);
             } else {
                 block_probs(sacc[0], pw[0], lsum[0]);
             }
             ATF_BLOCK_RESCALE(0, live1)
             if (live1) {
-                ATF_BLOCK_EDGES(1)
-                block_pv<NDB>(o, lt, vbase_lane, vz, 0, pw[0]);
+                ATF_BLOCK_EDGES(kp + 1, 1)
+                block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
                 block_probs(sacc[1], pw[1], lsum[1]);
                 ATF_BLOCK_RESCALE(1, false)
-                block_pv<NDB>(o, lt, vbase_lane, vz, 1, pw[1]);
+                block_pv<NDB>(o, lv, vbase_lane, vz, 1, pw[1]);
             } else {
-                block_pv<NDB>(o, lt, vbase_lane, vz, 0, pw[0]);
+                block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
             }
         }
 #undef ATF_BLOCK_EDGES
@@ -629,7 +641,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(AttnArgs a) {
         __syncthreads();
     }
 #undef ATF_TILE_LOAD
-#undef ATF_KOFF
 
     // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3)
     const float inv = 1.f / partner_sum(l_run);
@@ -1468,8 +1479,8 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
-    if (d == 128) prefill_bf16_kernel<128><<<n_wg, 256, 0, s>>>(a);
-    else prefill_bf16_kernel<64><<<n_wg, 256, 0, s>>>(a);
+    if (d == 128) prefill_bf16_kernel<128><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+    else prefill_bf16_kernel<64><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
