@@ -215,6 +215,64 @@ atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, v
                              atf_dtype dtype, void *workspace, size_t workspace_bytes,
                              uint64_t *skipped_out, atf_stream_t stream);
 
+/* ------------------------------------------------------- paged, ragged decode */
+
+/*
+ * The key-cache layout in pages, as a serving engine keeps it: a pool of pages
+ * of 64 tokens; sequence b's 64-token block c lives in page
+ * page_table[b * max_pages + c] (device int32 array [B][max_pages]), and
+ * sequence b holds seq_lens[b] tokens (device int32 array [B]).  Same method
+ * and source passages as atf_decode_kcache: the windows decide which key
+ * planes a block needs, so distant blocks read fewer bytes.
+ * Page p of the key pool (atf_paged_page_bytes bytes) holds, for each kv head
+ * h, one 64-key block in the plane layout of atf_decode_kcache at byte
+ * (p * Hkv + h) * (P/4 * 1024); page p of the value pool holds the 64 value
+ * rows of each kv head at byte (p * Hkv + h) * (64 * d * 2) + (j % 64) * d * 2.
+ * Both pools and both arrays are caller-owned device memory.  Page indices
+ * outside [0, num_pages) are clamped into it (no out-of-pool access; the
+ * result for such a table is unspecified).
+ */
+
+/* Bytes of one page of the key pool (equal to one page of the value pool);
+ * 0 for unsupported Hkv or d. */
+size_t atf_paged_page_bytes(int32_t Hkv, int32_t d);
+
+/* Bytes of workspace atf_decode_paged needs (per-split partials sized for the
+ * widest split count one sequence of max_len tokens can take, + counter);
+ * 0 for unsupported shapes. */
+size_t atf_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d);
+
+/*
+ * Writes tokens k_begin .. k_begin + n - 1 of every sequence into their
+ * pages: k, v [B][Hkv][n][d] (pre-RoPE keys, bf16), keys rotated at
+ * positions pos0 + k_begin + i.  Requires k_begin + n <= max_pages * 64;
+ * pos0 + max_pages * 64 + 1 < 2^31.  bf16 only (ATF_F32 is
+ * ATF_ERR_UNSUPPORTED).  Asynchronous on `stream`.
+ */
+atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpool,
+                           const int32_t *page_table, int32_t max_pages, int32_t num_pages,
+                           int32_t B, int32_t Hkv, int64_t n, int64_t k_begin, int32_t d,
+                           double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream);
+
+/*
+ * Ragged decode over the paged cache: sequence b's query q[b] ([B][Hq][1][d])
+ * sits at position pos0 + seq_lens[b] and attends to its seq_lens[b] keys.
+ * max_len (host) bounds every seq_lens[b] (values outside [1, max_len] are
+ * clamped into it) and sizes the split plan and the workspace:
+ * atf_decode_paged_workspace_bytes(B, Hq, Hkv, max_len, d).  Splits are
+ * planned on the device: each sequence takes a share of ~512 workgroups in
+ * proportion to its length, split into equal algorithmic bytes, so lengths
+ * and pages can change between calls without host work.  skipped_out as for atf_decode
+ * (summed over the ragged batch).  Errors: as atf_decode with S = max_len;
+ * max_len > max_pages * 64 or a misaligned/NULL array is ATF_ERR_INVALID_ARG.
+ */
+atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool, void *out,
+                            const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
+                            int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len,
+                            int32_t d, double rope_base, double alpha, int32_t causal, int64_t pos0,
+                            atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                            uint64_t *skipped_out, atf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@ EXPORTED = (
     "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
     "atf_prefill_attend", "atf_prefill_chunk", "atf_decode_workspace_bytes", "atf_decode",
     "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
+    "atf_paged_page_bytes", "atf_decode_paged_workspace_bytes", "atf_paged_write", "atf_decode_paged",
 )
 
 
@@ -84,6 +85,15 @@ def _lib():
     lib.atf_decode_kcache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, f64, f64, i32, i64,
                                       ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode_kcache.restype = ctypes.c_int
+    lib.atf_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+    lib.atf_decode_paged_workspace_bytes.restype = sz
+    lib.atf_paged_page_bytes.argtypes = [i32, i32]
+    lib.atf_paged_page_bytes.restype = sz
+    lib.atf_paged_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32, f64, i64, ctypes.c_int, vp]
+    lib.atf_paged_write.restype = ctypes.c_int
+    lib.atf_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+                                     ctypes.c_int, vp, sz, u64p, vp]
+    lib.atf_decode_paged.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -288,6 +298,60 @@ def atf_decode_kcache(q, kcache, v, out=None, *, S: int, rope_base: float, alpha
                                     int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                     ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode_kcache")
+    return (out, int(skipped.value)) if return_skipped else out
+
+
+def atf_paged_page_bytes(Hkv: int, d: int) -> int:
+    return int(_lib().atf_paged_page_bytes(Hkv, d))
+
+
+def atf_decode_paged_workspace_bytes(B: int, Hq: int, Hkv: int, max_len: int, d: int) -> int:
+    return int(_lib().atf_decode_paged_workspace_bytes(B, Hq, Hkv, max_len, d))
+
+
+def _dev_i32(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError("%s must be int32" % name)
+    return _dev(t, name)
+
+
+def atf_paged_write(k, v, kpool, vpool, page_table, *, k_begin: int, rope_base: float, pos0: int = 0):
+    """Write tokens k_begin.. of every sequence (k, v [B,Hkv,n,d]) into their pages.
+    page_table: int32 [B, max_pages] on the device; pools: one page = atf_paged_page_bytes."""
+    B, Hkv, n, d = k.shape
+    max_pages = page_table.shape[1]
+    num_pages = kpool.numel() * kpool.element_size() // atf_paged_page_bytes(Hkv, d)
+    _check(_lib().atf_paged_write(_dev(k, "k"), _dev(v, "v"), _dev(kpool, "kpool"), _dev(vpool, "vpool"),
+                                  _dev_i32(page_table, "page_table"), max_pages, num_pages, B, Hkv, n, int(k_begin),
+                                  d, float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
+           "atf_paged_write")
+
+
+def atf_decode_paged(q, kpool, vpool, page_table, seq_lens, out=None, *, max_len: int, rope_base: float,
+                     alpha: float, causal: int = 1, pos0: int = 0, ws=None, return_skipped: bool = False):
+    """Ragged decode over the paged cache: q [B,Hq,1,d]; seq_lens int32 [B] on the device."""
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence")
+    max_pages = page_table.shape[1]
+    Hkv = kpool.shape[1] if kpool.dim() >= 2 else None
+    if Hkv is None:
+        raise ValueError("kpool must be shaped [num_pages, Hkv, ...]")
+    num_pages = kpool.shape[0]
+    code = _dtype_code(q)
+    if out is None:
+        out = _torch().empty_like(q)
+    nbytes = atf_decode_paged_workspace_bytes(B, Hq, Hkv, max_len, d)
+    if ws is None:
+        ws = workspace(nbytes, q.device, "decode")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_decode_paged(_dev(q, "q"), _dev(kpool, "kpool"), _dev(vpool, "vpool"), _dev(out, "out"),
+                                   _dev_i32(page_table, "page_table"), _dev_i32(seq_lens, "seq_lens"), max_pages,
+                                   num_pages, B, Hq, Hkv, int(max_len), d, float(rope_base), float(alpha),
+                                   int(causal), int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                   ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_decode_paged")
     return (out, int(skipped.value)) if return_skipped else out
 
 

@@ -112,6 +112,25 @@ size_t decode_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d)
     return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
+// Paged, ragged decode: the batch shares a budget of ~512 workgroups per call
+// (one round of resident workgroups) in proportion to the sequences' lengths;
+// one sequence may take all of it.  The grid is that per-sequence maximum wide.
+void paged_plan(int32_t Hq, int32_t Hkv, int64_t max_len, int &budget, int &nsplit_max) {
+    const int group = Hq / Hkv;
+    const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
+    const int64_t units = (int64_t)Hkv * n_slabs;
+    const int64_t nchunks = (max_len + kKeyTile - 1) / kKeyTile;
+    const int64_t b = std::max<int64_t>(1, (512 + units - 1) / units);
+    budget = (int)b;
+    nsplit_max = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(b, kMaxSplits), nchunks));
+}
+
+size_t paged_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d) {
+    int budget, ns;
+    paged_plan(Hq, Hkv, max_len, budget, ns);
+    return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
+}
+
 // Algorithmic bytes of keys [0, j) for a query at distance S - j' from key j':
 // each key costs 2d bytes of value plus 4 bytes per kept pair.  Pair p (finite
 // W_p) is dropped for keys with S - j' > W_p, i.e. j' < S - W_p, so the dropped
@@ -471,6 +490,92 @@ atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, v
     a.n_slabs = plan.n_slabs;
     std::memcpy(a.split_start, plan.starts, sizeof(int) * (size_t)(plan.nsplit + 1));
     if (launch_decode_kcache_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(a.counter, skipped_out, s);
+}
+
+size_t atf_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d) {
+    if (check_shape(B, Hq, Hkv, max_len, d, 2.0, 1.0, 1, 0, ATF_BF16) != ATF_OK) return 0;
+    return paged_ws_bytes(B, Hq, Hkv, max_len, d);
+}
+
+size_t atf_paged_page_bytes(int32_t Hkv, int32_t d) {
+    if (Hkv < 1 || (d != 64 && d != 128)) return 0;
+    return (size_t)Hkv * kKeyTile * d * 2;
+}
+
+atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpool, const int32_t *page_table,
+                           int32_t max_pages, int32_t num_pages, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
+                           int32_t d, double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream) {
+    if (!k || !v || !kpool || !vpool || !page_table) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(kpool) || !aligned16(vpool) ||
+        ((uintptr_t)page_table & 3u) != 0)
+        return ATF_ERR_INVALID_ARG;
+    if (B < 1 || Hkv < 1 || n < 1 || k_begin < 0 || max_pages < 1 || num_pages < 1) return ATF_ERR_INVALID_ARG;
+    const int64_t cap = (int64_t)max_pages * kKeyTile;
+    if (k_begin + n > cap) return ATF_ERR_INVALID_ARG;
+    if (d < 2 || (d & 1)) return ATF_ERR_INVALID_ARG;
+    if (!std::isfinite(rope_base) || !(rope_base > 1.0)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
+    if (pos0 < 0 || pos0 + cap + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
+    PagedWriteArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.v = v;
+    a.kpool = kpool;
+    a.vpool = vpool;
+    a.page_table = page_table;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.n = (int)n;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    a.k_begin = k_begin;
+    a.pos0 = pos0;
+    theta_table(d, rope_base, a.theta);
+    return hip_status(launch_paged_write_bf16(a, d, (hipStream_t)stream));
+}
+
+atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool, void *out,
+                            const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages, int32_t num_pages,
+                            int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, double rope_base,
+                            double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                            size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+    atf_status st = check_shape(B, Hq, Hkv, max_len, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (!page_table || !seq_lens || ((uintptr_t)page_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
+        return ATF_ERR_INVALID_ARG;
+    if (max_pages < 1 || num_pages < 1 || max_len > (int64_t)max_pages * kKeyTile) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
+    if (!aligned16(workspace) || workspace_bytes < paged_ws_bytes(B, Hq, Hkv, max_len, d))
+        return ATF_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = kpool;
+    a.v = vpool;
+    a.out = out;
+    a.counter = (unsigned long long *)workspace;
+    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.S = (int)max_len;
+    a.page_table = page_table;
+    a.seq_lens = seq_lens;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    a.pos0 = pos0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    a.n_slabs = (a.group + kDecodeHeads - 1) / kDecodeHeads;
+    paged_plan(Hq, Hkv, max_len, a.split_budget, a.nsplit);
+    if (launch_decode_paged_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
     return read_counter(a.counter, skipped_out, s);
 }
 

@@ -65,6 +65,13 @@ struct DecodeArgs {
     unsigned long long *counter;
     int B, Hq, Hkv, group, S, nsplit, n_slabs;
     int cap;                          // key-cache layout: keys per (b, kv head) row of k and v
+    // paged key cache: k/v are page pools ([page][Hkv][64-key block]), key block
+    // c of sequence b lives in page page_table[b * max_pages + c]; sequence b
+    // holds seq_lens[b] keys (device arrays); splits are planned in-kernel
+    const int *page_table;
+    const int *seq_lens;
+    int max_pages, num_pages;
+    int split_budget;                 // paged: splits per (kv head, slab) shared by the batch, by length
     long long pos0;
     float scale_log2;
     int W[kMaxPairs];
@@ -85,6 +92,18 @@ struct KPackArgs {
 hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s);
 hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s);
 hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s);
+hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s);
+
+// Writes n tokens of every sequence into a paged key/value cache.
+struct PagedWriteArgs {
+    const void *k, *v;                // [B][Hkv][n][d] pre-RoPE keys, values
+    void *kpool, *vpool;              // [page][Hkv][64-key block] (keys in planes, values in rows)
+    const int *page_table;            // [B][max_pages]
+    int B, Hkv, n, max_pages, num_pages;
+    long long k_begin, pos0;          // token i of the call is token k_begin + i, at pos0 + k_begin + i
+    double theta[kMaxPairs];
+};
+hipError_t launch_paged_write_bf16(const PagedWriteArgs &a, int d, hipStream_t s);
 hipError_t launch_prep_f32(const PrepArgs &a, int d, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s);

@@ -1121,6 +1121,37 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
 }
 
+// Ragged batch: sequence b gets a share of the split budget proportional to
+// its length (at least 1, at most its 64-key chunks and the grid's width),
+// so short sequences do not hold back long ones.  Every wave returns the same.
+__device__ inline long long paged_total_len(const DecodeArgs &a) {
+    const int lane = threadIdx.x & 63;
+    unsigned long long tot = 0;
+    for (int i = lane; i < a.B; i += 64) tot += (unsigned long long)min(max(a.seq_lens[i], 1), a.S);
+    return (long long)wave_sum_u64(tot);
+}
+__device__ inline int paged_nsplit_of(const DecodeArgs &a, int b, long long tot) {
+    const long long L = min(max(a.seq_lens[b], 1), a.S);
+    const long long want = (L * a.split_budget + tot - 1) / tot;
+    const long long nch = (L + kKeyTile - 1) / kKeyTile;
+    return (int)max(1ll, min(want, min((long long)a.nsplit, nch)));
+}
+__device__ inline int paged_nsplit(const DecodeArgs &a, int b) { return paged_nsplit_of(a, b, paged_total_len(a)); }
+
+// Algorithmic bytes of keys [0, j) of a sequence of S keys (decode query after
+// them): 2d per value row plus 4 per kept pair, where pair p (finite W_p) is
+// dropped for the keys j' < S - W_p.  Lane p holds W_p (kWindowInf past the
+// table); every lane returns the sum.
+template <int D>
+__device__ inline long long dec_prefix_bytes(int j, int S, int w_lane) {
+    constexpr int P = D / 2;
+    const int lane = threadIdx.x & 63;
+    long long dropped = 0;
+    if (lane < P - 1 && w_lane != kWindowInf) dropped = min(j, max(0, S - w_lane));
+    dropped = (long long)wave_sum_u64((unsigned long long)dropped);
+    return (long long)j * (2 * D + 4 * P) - 4 * dropped;
+}
+
 // ============================================================================
 // Key-cache writer: rotates each key at its position and stores it in the
 // plane layout described below (one thread per (key, 4-pair plane): 8 bytes
@@ -1156,6 +1187,50 @@ __global__ __launch_bounds__(256) void kpack_bf16_kernel(KPackArgs a) {
 }
 
 // ============================================================================
+// Paged cache writer: token i of each sequence goes to the page holding its
+// 64-key block; keys rotated into the plane layout (as kpack_bf16_kernel),
+// values copied as rows.  One thread per (token, 16-byte unit).
+// grid (x, B*Hkv), block 256.
+// ============================================================================
+
+template <int D>
+__global__ __launch_bounds__(256) void paged_write_bf16_kernel(PagedWriteArgs a) {
+    constexpr int P = D / 2, NPL = P / 4, CHV = D / 8, U = NPL + CHV;
+    constexpr unsigned KPBLK = NPL * 1024;
+    const int bk = blockIdx.y, b = bk / a.Hkv, hk = bk % a.Hkv;
+    const long long total = (long long)a.n * U;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const int i = (int)(e / U), u = (int)(e % U);
+        const long long j = a.k_begin + i;
+        int page = a.page_table[(long long)b * a.max_pages + (int)(j / kKeyTile)];
+        page = min(max(page, 0), a.num_pages - 1);
+        const long long blk = (long long)page * a.Hkv + hk;
+        const long long src_row = ((long long)bk * a.n + i) * D;
+        if (u < NPL) {
+            const unsigned short *src = (const unsigned short *)a.k + src_row + 4 * u;
+            const u32x2 lo = *(const u32x2 *)src;
+            const u32x2 hi = *(const u32x2 *)(src + P);
+            unsigned r[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
+                const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
+                const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
+                float c, sn;
+                rope_cos_sin(a.pos0 + j, a.theta[4 * u + w], c, sn);
+                r[w] = pack_bf(x * c - y * sn, y * c + x * sn);
+            }
+            *(u32x4 *)((unsigned char *)a.kpool + blk * KPBLK + u * 1024 + (j % kKeyTile) * 16) =
+                (u32x4){r[0], r[1], r[2], r[3]};
+        } else {
+            const int c = u - NPL;
+            *(u32x4 *)((unsigned char *)a.vpool + blk * (kKeyTile * D * 2) + (j % kKeyTile) * (D * 2) + c * 16) =
+                *(const u32x4 *)((const unsigned short *)a.v + src_row + 8 * c);
+        }
+    }
+}
+
+// ============================================================================
 // Split-KV decode over a key cache laid out for the windows (bf16).  Keys are
 // stored rotated (at their own positions) in 64-key blocks of P/4 planes; plane
 // pg holds pairs 4pg .. 4pg+3 of the block's 64 keys, 16 bytes per key, word w
@@ -1172,7 +1247,7 @@ __global__ __launch_bounds__(256) void kpack_bf16_kernel(KPackArgs a) {
 // grid (nsplit, B*Hkv*n_slabs), block 256.
 // ============================================================================
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
@@ -1187,15 +1262,34 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char vbuf[4][VBYTES];
     __shared__ float wm[4][16], wl[4][16];
 
-    const int split = blockIdx.x;
+    // work item.  Paged: blockIdx.x walks the batch's splits (sequence b owns
+    // nsb_b consecutive ids); blockIdx.y is (kv head, slab).  Otherwise
+    // blockIdx.x is the split and blockIdx.y is (b, kv head, slab).
+    int split = blockIdx.x, b, hk, nsb = 0;
     const int slab = blockIdx.y % a.n_slabs;
-    const int bk = blockIdx.y / a.n_slabs;
-    const int b = bk / a.Hkv, hk = bk % a.Hkv;
+    if (PAGED) {
+        hk = blockIdx.y / a.n_slabs;
+        const long long tot = paged_total_len(a);
+        b = -1;
+        for (int i = 0, c0 = 0; i < a.B; ++i) {
+            const int n = paged_nsplit_of(a, i, tot);
+            if (split < c0 + n) { b = i; split -= c0; nsb = n; break; }
+            c0 += n;
+        }
+        if (b < 0) return;  // past the batch's splits (uniform)
+    } else {
+        const int bk0 = blockIdx.y / a.n_slabs;
+        b = bk0 / a.Hkv;
+        hk = bk0 % a.Hkv;
+    }
+    const int bk = b * a.Hkv + hk;
     const int h0 = hk * a.group + slab * H;
     const int nh = min(H, a.group - slab * H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = lane & 15, q = lane >> 4;
-    const long long qpos = a.pos0 + a.S;
+    // keys of this sequence (ragged when paged: clamped to [1, a.S], a.S = max_len)
+    const int S = PAGED ? min(max(a.seq_lens[b], 1), a.S) : a.S;
+    const long long qpos = a.pos0 + S;
 
     const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
 
@@ -1228,10 +1322,42 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    const int ks = a.split_start[split];
-    const int ke = min(a.split_start[split + 1], a.S);
-    const unsigned char *kpb = (const unsigned char *)a.k + (long long)bk * (a.cap / kKeyTile) * KPBLK;
-    const unsigned char *vbase = (const unsigned char *)a.v + (long long)bk * a.cap * VROW;
+    int ks, ke;
+    if (PAGED) {
+        // byte-balanced split boundaries of this sequence (same rule as the host
+        // planner): split s of nsb starts at the first 64-key chunk whose
+        // prefix of algorithmic bytes reaches s / nsb of the total; splits past
+        // nsb have no keys
+        const long long total = dec_prefix_bytes<D>(S, S, w_lane);
+        const int nchunks = (S + kKeyTile - 1) / kKeyTile;
+        auto start_of = [&](int sp) {
+            const long long target = total * min(sp, nsb) / nsb;
+            int lo = 0, hi = nchunks;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (dec_prefix_bytes<D>(min(S, mid * kKeyTile), S, w_lane) < target) lo = mid + 1; else hi = mid;
+            }
+            return lo * kKeyTile;
+        };
+        ks = start_of(split);
+        ke = min(start_of(split + 1), S);
+    } else {
+        ks = a.split_start[split];
+        ke = min(a.split_start[split + 1], S);
+    }
+    // key block c (64 keys) and its value rows
+    auto page_of = [&](int c) {
+        return min(max(a.page_table[(long long)b * a.max_pages + c], 0), a.num_pages - 1);
+    };
+    auto kblock = [&](int c) {
+        return (const unsigned char *)a.k +
+               (PAGED ? ((long long)page_of(c) * a.Hkv + hk) : ((long long)bk * (a.cap / kKeyTile) + c)) * KPBLK;
+    };
+    auto vblock = [&](int c) {
+        return (const unsigned char *)a.v +
+               (PAGED ? ((long long)page_of(c) * a.Hkv + hk) : ((long long)bk * (a.cap / kKeyTile) + c)) *
+                   (kKeyTile * VROW);
+    };
     unsigned char *vb = vbuf[wave];
 
     // Value rows are staged with 16-byte chunks swizzled: row r, chunk c at
@@ -1247,11 +1373,12 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 #define DEC_LOAD_V(jc_)                                                                 \
     {                                                                                 \
         const int nrow_ = min(CK, ke - (jc_));  /* rows past the split repeat its last row */ \
+        const unsigned char *vb_ = vblock((jc_) / kKeyTile);                          \
         _Pragma("unroll") for (int m = 0; m < NVP; ++m) {                             \
             const int row_ = VR * m + vlr;                                            \
             const int c_ = (lane % CHV) ^ vsw(row_);                                  \
-            const int grow_ = (jc_) + min(row_, nrow_ - 1);                           \
-            vreg[m] = *(const u32x4 *)(vbase + (long long)grow_ * VROW + c_ * 16);    \
+            const int brow_ = (jc_) % kKeyTile + min(row_, nrow_ - 1);                \
+            vreg[m] = *(const u32x4 *)(vb_ + brow_ * VROW + c_ * 16);                 \
         }                                                                             \
     }
     // this lane's transposed-read byte address for output block db, key group hh
@@ -1275,8 +1402,8 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     // windows that fall inside the chunk's distance range.
 #define DEC_CHUNK_KEYS(jc_, smin_, ps0_, ps1_)                                          \
     {                                                                                 \
-        const int d_near_ = a.S - min((jc_) + CK - 1, ke - 1);                        \
-        const int d_far_ = a.S - (jc_);                                               \
+        const int d_near_ = S - min((jc_) + CK - 1, ke - 1);                          \
+        const int d_far_ = S - (jc_);                                                 \
         const int p_near_ = __builtin_popcountll(__ballot(w_lane < d_near_));         \
         smin_ = p_near_ >> 4;                                                         \
         pmin = p_near_ >> 2;                                                          \
@@ -1285,8 +1412,8 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         for (int pp = p_near_; pp < P - 1; ++pp) {                                    \
             const int wpp = __builtin_amdgcn_readlane(w_lane, pp);                    \
             if (wpp >= d_far_) break;                                                 \
-            ps0_ += (wpp < a.S - ((jc_) + t)) ? 1 : 0;                                \
-            ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;                           \
+            ps0_ += (wpp < S - ((jc_) + t)) ? 1 : 0;                                  \
+            ps1_ += (wpp < S - ((jc_) + 16 + t)) ? 1 : 0;                             \
         }                                                                             \
         if ((jc_) + t >= ke) ps0_ = P;                                                \
         if ((jc_) + 16 + t >= ke) ps1_ = P;                                           \
@@ -1300,7 +1427,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 #define DEC_KOFF(pg_, row_) (((pg_) >= pmin) ? (unsigned)((pg_) * 1024 + (row_) * 16) : KPBLK)
 #define DEC_LOAD_K(jc_)                                                                 \
     {                                                                                 \
-        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kpb + (long long)((jc_) / kKeyTile) * KPBLK, KPBLK); \
+        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kblock((jc_) / kKeyTile), KPBLK);   \
         _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
             const int row_ = min((jc_) + 16 * g + t, ke - 1) % kKeyTile;               \
             _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i)                  \
@@ -1324,7 +1451,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int m = 0; m < NVP; ++m) *(u32x4 *)(vb + m * 1024 + lane * 16) = vreg[m];
         if (jn < ke) DEC_LOAD_V(jn);
-        const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kpb + (long long)(j0 / kKeyTile) * KPBLK, KPBLK);
+        const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblock(j0 / kKeyTile), KPBLK);
 
         f32x4_t sc[2];
 #pragma unroll
@@ -1441,14 +1568,15 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // grid B*Hq, block D.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
     const int row = blockIdx.x, c = threadIdx.x;
     const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
+    const int ns = PAGED ? paged_nsplit(a, row / a.Hq) : a.nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
     float num = 0.f, den = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
+    for (int s = 0; s < ns; ++s) {
         const float ms = pr[s * (D + 2) + D];
         if (ms == -INFINITY) continue;
         const float f = fast_exp2(ms - M);
@@ -1498,8 +1626,8 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     else decode_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d == 128) decode_combine_kernel<128><<<a.B * a.Hq, 128, 0, s>>>(a);
-    else decode_combine_kernel<64><<<a.B * a.Hq, 64, 0, s>>>(a);
+    if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
+    else decode_combine_kernel<64, false><<<a.B * a.Hq, 64, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -1512,15 +1640,38 @@ hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_paged_write_bf16(const PagedWriteArgs &a, int d, hipStream_t s) {
+    const long long total = (long long)a.n * (d / 8 + d / 8);
+    const unsigned gx = (unsigned)std::min<long long>((total + 255) / 256, 65535);
+    dim3 grid(gx, (unsigned)(a.B * a.Hkv));
+    if (d == 128) paged_write_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    else paged_write_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s) {
+    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
+    // paged: x walks the batch's splits (at most budget + B of them), y = (kv head, slab)
+    grid = dim3((unsigned)(a.split_budget + a.B), (unsigned)(a.Hkv * a.n_slabs));
+    if (d == 128) decode_kcache_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else decode_kcache_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d == 128) decode_combine_kernel<128, true><<<a.B * a.Hq, 128, 0, s>>>(a);
+    else decode_combine_kernel<64, true><<<a.B * a.Hq, 64, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
-    if (d == 128) decode_kcache_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
-    else decode_kcache_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    if (d == 128) decode_kcache_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
+    else decode_kcache_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d == 128) decode_combine_kernel<128><<<a.B * a.Hq, 128, 0, s>>>(a);
-    else decode_combine_kernel<64><<<a.B * a.Hq, 64, 0, s>>>(a);
+    if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
+    else decode_combine_kernel<64, false><<<a.B * a.Hq, 64, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -217,3 +217,54 @@ def test_kcache_decode_rejects(lib, kw, expect):
 ])
 def test_kcache_decode_rejects_layout(lib, kw, expect):
     assert _call_kcache(lib, **kw) == expect
+
+
+def test_paged_page_bytes(lib):
+    assert atf.atf_paged_page_bytes(4, 128) == 4 * 64 * 128 * 2
+    assert atf.atf_paged_page_bytes(1, 64) == 64 * 64 * 2
+    assert atf.atf_paged_page_bytes(0, 128) == 0 and atf.atf_paged_page_bytes(2, 96) == 0
+
+
+def _call_pwrite(lib, **kw):
+    args = dict(k=16, v=32, kp=48, vp=64, pt=128, max_pages=4, num_pages=8, B=2, Hkv=2, n=10, k_begin=0, d=128,
+                base=1e6, pos0=0, dtype=atf.ATF_BF16, stream=None)
+    args.update(kw)
+    return lib.atf_paged_write(*(ctypes.c_void_p(args[x]) for x in ("k", "v", "kp", "vp", "pt")),
+                               args["max_pages"], args["num_pages"], args["B"], args["Hkv"], args["n"],
+                               args["k_begin"], args["d"], args["base"], args["pos0"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=None), bnd.ATF_ERR_INVALID_ARG), (dict(pt=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(pt=130), bnd.ATF_ERR_INVALID_ARG), (dict(vp=72), bnd.ATF_ERR_INVALID_ARG),
+    (dict(n=0), bnd.ATF_ERR_INVALID_ARG), (dict(k_begin=250, n=10), bnd.ATF_ERR_INVALID_ARG),
+    (dict(max_pages=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=96), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(base=0.5), bnd.ATF_ERR_INVALID_ARG), (dict(pos0=-3), bnd.ATF_ERR_INVALID_ARG),
+])
+def test_paged_write_rejects(lib, kw, expect):
+    assert _call_pwrite(lib, **kw) == expect
+
+
+def _call_pdecode(lib, **kw):
+    args = dict(q=16, kp=32, vp=48, out=64, pt=128, sl=256, max_pages=4, num_pages=8, B=2, Hq=4, Hkv=2,
+                max_len=200, d=128, base=1e6, alpha=1.0, causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096,
+                ws_bytes=1, skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_decode_paged(*(ctypes.c_void_p(args[x]) for x in ("q", "kp", "vp", "out", "pt", "sl")),
+                                args["max_pages"], args["num_pages"], args["B"], args["Hq"], args["Hkv"],
+                                args["max_len"], args["d"], args["base"], args["alpha"], args["causal"],
+                                args["pos0"], args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"],
+                                args["skipped"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), bnd.ATF_ERR_INVALID_ARG), (dict(sl=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(sl=258), bnd.ATF_ERR_INVALID_ARG), (dict(max_len=257), bnd.ATF_ERR_INVALID_ARG),
+    (dict(max_len=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(Hq=5), bnd.ATF_ERR_INVALID_ARG), (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(causal=0), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG), (dict(ws_bytes=1), bnd.ATF_ERR_WORKSPACE),
+])
+def test_paged_decode_rejects(lib, kw, expect):
+    assert _call_pdecode(lib, **kw) == expect
