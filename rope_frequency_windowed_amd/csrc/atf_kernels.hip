@@ -1349,15 +1349,14 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     auto page_of = [&](int c) {
         return min(max(a.page_table[(long long)b * a.max_pages + c], 0), a.num_pages - 1);
     };
-    auto kblock = [&](int c) {
-        return (const unsigned char *)a.k +
-               (PAGED ? ((long long)page_of(c) * a.Hkv + hk) : ((long long)bk * (a.cap / kKeyTile) + c)) * KPBLK;
+    // block slot of key block c in the key / value arrays; when paged, each
+    // chunk's slot is looked up two chunks ahead so the table read is off the
+    // load path
+    auto slot_of = [&](int c) -> long long {
+        return PAGED ? ((long long)page_of(c) * a.Hkv + hk) : ((long long)bk * (a.cap / kKeyTile) + c);
     };
-    auto vblock = [&](int c) {
-        return (const unsigned char *)a.v +
-               (PAGED ? ((long long)page_of(c) * a.Hkv + hk) : ((long long)bk * (a.cap / kKeyTile) + c)) *
-                   (kKeyTile * VROW);
-    };
+    auto kblock = [&](long long sl) { return (const unsigned char *)a.k + sl * KPBLK; };
+    auto vblock = [&](long long sl) { return (const unsigned char *)a.v + sl * (kKeyTile * VROW); };
     unsigned char *vb = vbuf[wave];
 
     // Value rows are staged with 16-byte chunks swizzled: row r, chunk c at
@@ -1370,10 +1369,10 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     const int vlr = lane / CHV;
     auto vsw = [](int r) { return 2 * (r % (CHV / 2)); };
     u32x4 vreg[NVP];
-#define DEC_LOAD_V(jc_)                                                                 \
+#define DEC_LOAD_V(jc_, sl_)                                                            \
     {                                                                                 \
         const int nrow_ = min(CK, ke - (jc_));  /* rows past the split repeat its last row */ \
-        const unsigned char *vb_ = vblock((jc_) / kKeyTile);                          \
+        const unsigned char *vb_ = vblock(sl_);                                       \
         _Pragma("unroll") for (int m = 0; m < NVP; ++m) {                             \
             const int row_ = VR * m + vlr;                                            \
             const int c_ = (lane % CHV) ^ vsw(row_);                                  \
@@ -1425,9 +1424,9 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     // Rows past the split repeat its last key.
     constexpr int SPRE = (NSTEP >= 2) ? NSTEP - 2 : 0;
 #define DEC_KOFF(pg_, row_) (((pg_) >= pmin) ? (unsigned)((pg_) * 1024 + (row_) * 16) : KPBLK)
-#define DEC_LOAD_K(jc_)                                                                 \
+#define DEC_LOAD_K(jc_, sl_)                                                            \
     {                                                                                 \
-        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kblock((jc_) / kKeyTile), KPBLK);   \
+        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kblock(sl_), KPBLK);              \
         _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
             const int row_ = min((jc_) + 16 * g + t, ke - 1) % kKeyTile;               \
             _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i)                  \
@@ -1438,20 +1437,24 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     int j0 = ks + wave * CK;
     int s_min = 0, ps0 = P, ps1 = P, pmin = 0;
     u32x4 kreg[2][NSTEP - SPRE];
+    long long sl_cur = 0, sl_nxt = 0;
     if (j0 < ke) {
-        DEC_LOAD_V(j0);
+        sl_cur = slot_of(j0 / kKeyTile);
+        if (j0 + 4 * CK < ke) sl_nxt = slot_of((j0 + 4 * CK) / kKeyTile);
+        DEC_LOAD_V(j0, sl_cur);
         DEC_CHUNK_KEYS(j0, s_min, ps0, ps1);
-        DEC_LOAD_K(j0);
+        DEC_LOAD_K(j0, sl_cur);
     }
     for (; j0 < ke; j0 += 4 * CK) {
         const int jn = j0 + 4 * CK;
+        const long long sl_nn = (jn + 4 * CK < ke) ? slot_of((jn + 4 * CK) / kKeyTile) : 0;
         // this chunk's values to LDS (the previous chunk's transposed reads,
         // earlier in this wave's LDS order, are done with the buffer), then
         // the next chunk's values into the freed registers
 #pragma unroll
         for (int m = 0; m < NVP; ++m) *(u32x4 *)(vb + m * 1024 + lane * 16) = vreg[m];
-        if (jn < ke) DEC_LOAD_V(jn);
-        const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblock(j0 / kKeyTile), KPBLK);
+        if (jn < ke) DEC_LOAD_V(jn, sl_nxt);
+        const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblock(sl_cur), KPBLK);
 
         f32x4_t sc[2];
 #pragma unroll
@@ -1481,7 +1484,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         // next chunk's keys: bookkeeping and the prefetched key pieces
         if (jn < ke) {
             DEC_CHUNK_KEYS(jn, s_min, ps0, ps1);
-            DEC_LOAD_K(jn);
+            DEC_LOAD_K(jn, sl_nxt);
         }
 
         // online softmax per head slot t (log2 units, lazy reference)
@@ -1522,6 +1525,8 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        sl_cur = sl_nxt;
+        sl_nxt = sl_nn;
     }
 #undef DEC_CHUNK_KEYS
 #undef DEC_LOAD_K
