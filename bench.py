@@ -4,17 +4,18 @@
 One step = one causal prefill of S=131072 tokens (B=1, Hq=28, Hkv=4, d=128,
 RoPE base 1e6, alpha=1, bf16 with fp32 accumulation) followed by one decode
 step (B=8 sequences, one query each after a 262144-key cache, same heads)
-over the standard [S][d] cache and one over the windowed key-cache layout,
+over the standard [S][d] cache, one over the windowed key-cache layout and one
+over that layout in shuffled 64-token pages,
 inputs iid N(0,1) from fixed seeds, already resident in HBM.
 
 Printed: one JSON line.  `value` is prefill tokens/s; the `roofline` object
 is for the dominant kernel (the prefill attention kernel, MFMA-bound; the
 algorithmic flops count only the pair products the windows keep plus P.V);
-`decode` and `decode_kcache` carry the decode steps' algorithmic HBM rates
+`decode`, `decode_kcache` and `decode_paged` carry the decode steps' algorithmic HBM rates
 against their roofline; `cpu_baseline` is the fp64 oracle timed on a bounded
 sample on the host.
 
-  python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache|paged] [--no-cpu]
   python bench.py --copy-probe      (plain copy kernel of known size, for the
                                      HBM-counter scale factor)
 """
@@ -38,6 +39,7 @@ KERNEL_SRC = os.path.join(ROOT, "rope_frequency_windowed_amd", "csrc", "atf_kern
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_counters.txt")
 DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kv262144_counters.txt")
 KCACHE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kcache_kv262144_counters.txt")
+PAGED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_paged_kv262144_counters.txt")
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
@@ -144,7 +146,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["prefill", "decode", "kcache"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "kcache", "paged"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -167,6 +169,7 @@ def main():
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
     do_kcache = args.only in (None, "kcache")
+    do_paged = args.only in (None, "paged")
 
     if do_prefill:
         P = PREFILL
@@ -198,6 +201,23 @@ def main():
                              dtype=torch.uint8, device=dev)
         atf.atf_decode_pack_k(kk, kcache, k_begin=0, cap=D["S"], rope_base=D["base"])
         del kk
+    if do_paged:
+        import numpy as np
+        D = DECODE
+        pq, pk, pv = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
+        pout = torch.empty_like(pq)
+        n_pages = D["B"] * D["S"] // 64
+        # pages of the 8 sequences dealt out in a seeded random order over the pool
+        ptab = torch.as_tensor(np.random.default_rng(0).permutation(n_pages).reshape(D["B"], -1).astype(np.int32),
+                               device=dev)
+        page_b = atf.atf_paged_page_bytes(D["Hkv"], D["d"])
+        kpool = torch.empty(n_pages, D["Hkv"], page_b // D["Hkv"], dtype=torch.uint8, device=dev)
+        vpool = torch.empty_like(kpool)
+        atf.atf_paged_write(pk, pv, kpool, vpool, ptab, k_begin=0, rope_base=D["base"])
+        del pk, pv
+        plens = torch.full((D["B"],), D["S"], dtype=torch.int32, device=dev)
+        pws = torch.empty(atf.atf_decode_paged_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
+                          dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -223,12 +243,19 @@ def main():
                                   alpha=DECODE["alpha"], ws=kws)
             if ev is not None:
                 ev[6].record(stream)
+        if do_paged:
+            if ev is not None:
+                ev[7].record(stream)
+            atf.atf_decode_paged(pq, kpool, vpool, ptab, plens, pout, max_len=DECODE["S"], rope_base=DECODE["base"],
+                                 alpha=DECODE["alpha"], ws=pws)
+            if ev is not None:
+                ev[8].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -282,6 +309,20 @@ def main():
         log("decode (key-cache layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
             % (kc_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
         if not do_prefill and not do_decode:
+            res["value"], res["unit"] = gbs, "GB/s"
+    if do_paged:
+        pg_ms = sum(e[7].elapsed_time(e[8]) for e in events) / args.steps
+        nbytes = decode_algorithmic_bytes(atf, **DECODE)
+        gbs = nbytes / (pg_ms * 1e-3) / 1e9
+        res["decode_paged"] = {
+            "value": gbs, "unit": "GB/s", "ms": pg_ms, "tok_per_s": DECODE["B"] / (pg_ms * 1e-3),
+            "layout": "key-cache layout in 64-token pages, seeded random page table, lengths on the device",
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                         "traffic": read_traffic(PAGED_COUNTERS_FILE)}}
+        log("decode (paged key cache): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
+            % (pg_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+        if args.only == "paged":
             res["value"], res["unit"] = gbs, "GB/s"
     res["config"] = config
     if do_prefill and not args.no_cpu:

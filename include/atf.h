@@ -37,8 +37,11 @@
  *     check runs on the host before anything is queued.
  *   - Supported: d in {64, 128}; Hq % Hkv == 0; Hq/Hkv <= 64; S >= 1;
  *     0 <= pos0 and pos0 + S + 1 < 2^31; alpha > 0 (finite or +inf; +inf
- *     means no window); rope_base > 1 and finite; causal == 1 (0 returns
- *     ATF_ERR_UNSUPPORTED).
+ *     means no window); rope_base > 1 and finite; causal in {0, 1}.
+ *   - causal = 1: query i sees the keys at or before its position.  causal = 0
+ *     (prefill): every key, the windows applying to the distance |i - j| (no
+ *     page fixes the non-causal case; it is the plain reading of a distance
+ *     window).  Decode is the same either way: its query follows every key.
  */
 #ifndef ATF_H
 #define ATF_H
@@ -55,7 +58,7 @@ typedef struct ihipStream_t *atf_stream_t; /* same object as hipStream_t */
 typedef enum {
     ATF_OK = 0,
     ATF_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or value */
-    ATF_ERR_UNSUPPORTED = 2, /* valid but not implemented (d, causal=0, ...) */
+    ATF_ERR_UNSUPPORTED = 2, /* valid but not implemented (d, dtype, ...) */
     ATF_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
     ATF_ERR_HIP = 4          /* a HIP launch or copy failed */
 } atf_status;
@@ -79,7 +82,9 @@ atf_status atf_window_table(int32_t d, double rope_base, double alpha, int64_t *
  * Closed-form number of dropped (query, key, pair) terms for ONE (batch,
  * query-head) pair:  causal prefill of S tokens (is_decode = 0):
  * sum_p n_p (n_p + 1) / 2 with n_p = max(0, S - 1 - W_p);  decode of one query
- * after S keys (is_decode = 1): sum_p max(0, S - W_p).  causal must be 1.
+ * after S keys (is_decode = 1): sum_p max(0, S - W_p).  causal = 0 doubles
+ * the prefill count (the keys after each query, at the same distances) and
+ * leaves decode unchanged.
  */
 atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, double alpha,
                                      int32_t causal, int32_t is_decode, uint64_t *per_head_out);
@@ -129,7 +134,8 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
 
 /*
  * Chunked prefill: Sq new query tokens after a prefix of Sk - Sq cached
- * tokens, all attending causally to the Sk keys (prefix + chunk).
+ * tokens, attending to the Sk keys (prefix + chunk): causally (causal = 1)
+ * or to all of them with windows on |i - j| (causal = 0).
  *   q, out [B][Hq][Sq][d];  k, v [B][Hkv][Sk][d] (pre-RoPE, prefix first).
  * Key j sits at pos0 + j; query i at pos0 + Sk - Sq + i, so query i sees keys
  * 0 .. Sk - Sq + i and the windows apply to that distance exactly as in

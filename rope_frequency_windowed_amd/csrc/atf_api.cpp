@@ -75,7 +75,6 @@ atf_status check_shape(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
     if (pos0 < 0 || pos0 + S + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
     if (Hq / Hkv > 64) return ATF_ERR_UNSUPPORTED;
-    if (causal == 0) return ATF_ERR_UNSUPPORTED;
     return ATF_OK;
 }
 
@@ -191,7 +190,7 @@ atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) 
 // at positions pos0 + j.  Shapes are checked by the caller.
 atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
                        int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, double rope_base, double alpha,
-                       int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                       int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
                        uint64_t *skipped_out, hipStream_t s) {
     if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
     if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
@@ -211,6 +210,7 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
     a.Sk_pad = (int)padded_keys(Sk);
     a.q_pos0 = pos0 + (Sk - Sq);
     a.k_pos0 = pos0;
+    a.causal = causal;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
@@ -262,7 +262,7 @@ atf_status atf_window_table(int32_t d, double rope_base, double alpha, int64_t *
 atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, double alpha,
                                      int32_t causal, int32_t is_decode, uint64_t *per_head_out) {
     if (!per_head_out || S < 1 || (is_decode != 0 && is_decode != 1)) return ATF_ERR_INVALID_ARG;
-    if (causal != 1) return causal == 0 ? ATF_ERR_UNSUPPORTED : ATF_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return ATF_ERR_INVALID_ARG;
     std::vector<int64_t> W((size_t)std::max(1, d / 2));
     atf_status st = atf_window_table(d, rope_base, alpha, W.data());
     if (st != ATF_OK) return st;
@@ -274,6 +274,9 @@ atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, dou
         if (n <= 0) continue;
         total += is_decode ? (uint64_t)n : (uint64_t)n * (uint64_t)(n + 1) / 2u;
     }
+    // without the causal mask a prefill query also sees the keys after it, at
+    // the same distances: twice the count (decode has no key after its query)
+    if (causal == 0 && !is_decode) total *= 2u;
     *per_head_out = total;
     return ATF_OK;
 }
@@ -318,7 +321,7 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
                               size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
-    return attend_impl(q, k, v, out, B, Hq, Hkv, S, S, d, rope_base, alpha, pos0, dtype, workspace,
+    return attend_impl(q, k, v, out, B, Hq, Hkv, S, S, d, rope_base, alpha, causal, pos0, dtype, workspace,
                        workspace_bytes, skipped_out, stream);
 }
 
@@ -352,7 +355,7 @@ atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *
     st = atf_prefill_prepare_kv(k, v, B, Hkv, Sk, d, rope_base, pos0, dtype, workspace, workspace_bytes,
                                 stream);
     if (st != ATF_OK) return st;
-    return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_base, alpha, pos0, dtype, workspace,
+    return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_base, alpha, causal, pos0, dtype, workspace,
                        workspace_bytes, skipped_out, (hipStream_t)stream);
 }
 
@@ -389,6 +392,7 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
         a.Sk_pad = (int)S;
         a.q_pos0 = pos0 + S;
         a.k_pos0 = pos0;
+        a.causal = 1;  // the query follows every key: both settings see all of them
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
         window_table_i32(d, rope_base, alpha, a.W);
         theta_table(d, rope_base, a.theta);

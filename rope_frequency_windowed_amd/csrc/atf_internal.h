@@ -49,6 +49,7 @@ struct AttnArgs {
     int B, Hq, Hkv, group;
     int Sq, Sk, Sk_pad;               // query rows, keys, padded keys
     long long q_pos0, k_pos0;         // position of query 0 and key 0
+    int causal;                       // 1: keys at or before the query; 0: all keys, windows on |i - j|
     int n_qtiles, n_groups;           // work decomposition
     float scale_log2;                 // log2(e) / sqrt(d)
     int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)

@@ -362,7 +362,7 @@ __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, 
 #undef ATF_CHAIN
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill_bf16_kernel(AttnArgs a) {
     constexpr int P = D / 2;
     constexpr int NW = kPrefillWaves;  // waves per workgroup (two per SIMD)
@@ -435,7 +435,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 
     const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
-    const int last_key = min(a.Sk - 1, q0k + kQueryTile - 1);
+    // causal: keys up to the workgroup's last query; otherwise every key, the
+    // windows applying to |i - j|
+    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + kQueryTile - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
@@ -461,7 +463,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 #define ATF_TILE_LOAD(kt_, buf_)                                                           \
     {                                                                                      \
         const int j0_ = (kt_) * KT;                                                        \
-        const int dmin_wg_ = max(0, q0k - (j0_ + KT - 1));                                 \
+        const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
+                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + kQueryTile - 1))); \
         const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
         /* a key chunk below c_min is not fetched: its offset is past the buffer's end */ \
         const unsigned koff_ = (k_chunk >= c_min_) ? k_goff : KT_BYTES;                    \
@@ -527,9 +530,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 #pragma unroll
         for (int kb = 0; kb < NB; ++kb) {
             const int jb = j0 + 32 * kb;
-            live[kb] = jb <= i0k + 31;
-            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < max(0, i0k - (jb + 31))));
-            p_full[kb] = __builtin_popcountll(__ballot(w_lane < i0k + 31 - jb));
+            // distances i - j of the block span [i0k - jb - 31, i0k + 31 - jb]
+            const int dlo = i0k - jb - 31, dhi = i0k + 31 - jb;
+            live[kb] = CAUSAL ? dhi >= 0 : jb < a.Sk;
+            const int amin = CAUSAL ? max(0, dlo) : max(0, max(dlo, -dhi));
+            const int amax = CAUSAL ? dhi : max(dhi, -dlo);
+            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < amin));
+            p_full[kb] = __builtin_popcountll(__ballot(w_lane < amax));
         }
 
         // boundary pairs (one rank-2 MFMA each, added where the distance is
@@ -537,13 +544,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 #define ATF_BLOCK_EDGES(kb, sl)                                                                   \
         {                                                                                         \
             const int jb = j0 + 32 * (kb);                                                        \
-            const bool diag = jb + 31 > i0k;                                                      \
+            /* causal: some key may follow some query; otherwise: some key is past Sk */          \
+            const bool diag = CAUSAL ? jb + 31 > i0k : jb + 31 >= a.Sk;                           \
             const unsigned kbase = kbase_lane + 32u * (kb) * (CH * 16);                           \
+            /* element r holds key jb + koff0 + c_r, c_r = 8(r/4) + r%4, at distance dq - c_r;    \
+               it is a real (causal) key iff c_r < vlim */                                        \
+            const int dq = my_qk - koff0 - jb;                                                    \
+            const int vlim = CAUSAL ? dq + 1 : a.Sk - jb - koff0;                                 \
             if (p_lo[kb] > 0) {                                                                   \
                 if (!diag) {                                                                      \
                     skipped_u += (unsigned long long)p_lo[kb] * 16u * n_valid;                    \
                 } else if (q_valid) {                                                             \
-                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(my_qk - koff0 - jb + 1); \
+                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(vlim);         \
                 }                                                                                 \
             }                                                                                     \
             if (p_lo[kb] < p_full[kb]) {                                                          \
@@ -560,20 +572,24 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                             kw.w = (pb + 3 == p) ? kraw.w : 0u;                                   \
                             const f32x16_t tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(          \
                                 __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);        \
-                            /* element r holds key jb + koff0 + c_r, c_r = 8(r/4) + r%4, at    \
-                               distance dq - c_r; it keeps pair p iff c_r >= dq - W_p */          \
-                            const int dq = my_qk - koff0 - jb;                                    \
-                            const int lim = dq - __builtin_amdgcn_readlane(w_lane, p);            \
-                            _Pragma("unroll") for (int r = 0; r < 16; ++r)                        \
-                                sacc[sl][r] += (8 * (r >> 2) + (r & 3) >= lim) ? tp[r] : 0.f;     \
-                            if (q_valid) skipped += (unsigned)keys_below(min(lim, dq + 1));       \
+                            /* pair p is kept iff |dq - c_r| <= W_p: lim <= c_r <= him */      \
+                            const int wp = __builtin_amdgcn_readlane(w_lane, p);                  \
+                            const int lim = dq - wp, him = CAUSAL ? dq : dq + wp;                 \
+                            _Pragma("unroll") for (int r = 0; r < 16; ++r) {                      \
+                                const int c = 8 * (r >> 2) + (r & 3);                             \
+                                sacc[sl][r] += (c >= lim && (CAUSAL || c <= him)) ? tp[r] : 0.f;  \
+                            }                                                                     \
+                            if (q_valid)                                                          \
+                                skipped += (unsigned)(keys_below(min(lim, vlim)) +                \
+                                                      (CAUSAL ? 0 : keys_below(vlim) -           \
+                                                                     keys_below(min(vlim, him + 1)))); \
                         }                                                                         \
                     }                                                                             \
                 }                                                                                 \
             }                                                                                     \
             if (diag) {                                                                           \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r)                                    \
-                    if (jb + 8 * (r >> 2) + koff0 + (r & 3) > my_qk) sacc[sl][r] = -INFINITY;     \
+                    if (8 * (r >> 2) + (r & 3) >= vlim) sacc[sl][r] = -INFINITY;                  \
             }                                                                                     \
         }
 
@@ -695,9 +711,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
     }
     const float *kh = (const float *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk * D;  // raw keys
     const float *vh = (const float *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk * D;
-    // last key any query of this block may see
+    // last key any query of this block may see (every key when not causal)
     const long long qpos_last = a.q_pos0 + min(a.Sq, qblk0 + 64) - 1;
-    const long long kend_ll = min((long long)a.Sk, qpos_last - a.k_pos0 + 1);
+    const long long kend_ll = a.causal ? min((long long)a.Sk, qpos_last - a.k_pos0 + 1) : (long long)a.Sk;
     const int kend = (int)max(0ll, kend_ll);
 
     float o[D];
@@ -726,8 +742,9 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
         __syncthreads();
         const int nk = min(TK, kend - j0);
         for (int jj = 0; jj < nk; ++jj) {
-            const long long delta = qpos - (a.k_pos0 + j0 + jj);
-            if (!valid || delta < 0) continue;
+            long long delta = qpos - (a.k_pos0 + j0 + jj);
+            if (!valid || (a.causal && delta < 0)) continue;
+            if (delta < 0) delta = -delta;  // windows on |i - j| when not causal
             float s = 0.f;
             int ndrop = 0;
 #pragma unroll
@@ -1612,8 +1629,13 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
-    if (d == 128) prefill_bf16_kernel<128><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
-    else prefill_bf16_kernel<64><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+    if (a.causal) {
+        if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+    } else {
+        if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

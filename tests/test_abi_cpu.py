@@ -55,6 +55,21 @@ def test_closed_form_matches_oracle(lib, orc, S, d, base, alpha):
             orc.skipped_closed_form(S, d, base, alpha, decode=bool(dec))
 
 
+@pytest.mark.parametrize("S", [1, 2, 9, 40, 100])
+@pytest.mark.parametrize("d,base,alpha", [(16, 10.0, 1.0), (8, 3.0, 0.5), (16, 10.0, math.inf)])
+def test_noncausal_closed_form_matches_oracle(lib, orc, S, d, base, alpha):
+    """Non-causal prefill: the library's closed form equals the oracle's
+    enumeration of (i, j, p) with |i - j| > W_p, and twice the causal count;
+    decode is unchanged."""
+    rng = np.random.default_rng(S)
+    q = rng.standard_normal((1, 1, S, d)).astype(np.float32)
+    k = rng.standard_normal((1, 1, S, d)).astype(np.float32)
+    _, cnt = orc.attention(q, k, k, base=base, alpha=alpha, causal=False)
+    got = atf.atf_skipped_pair_products(S, d, base, alpha, 0, 0)
+    assert got == cnt == 2 * atf.atf_skipped_pair_products(S, d, base, alpha, 1, 0)
+    assert atf.atf_skipped_pair_products(S, d, base, alpha, 0, 1) == atf.atf_skipped_pair_products(S, d, base, alpha, 1, 1)
+
+
 def test_known_counts(lib):
     assert atf.atf_skipped_pair_products(256, 64, 1e4, 1.0) == 270074
 
@@ -98,7 +113,7 @@ BAD = [
     (dict(alpha=0.0), bnd.ATF_ERR_INVALID_ARG),
     (dict(alpha=-2.0), bnd.ATF_ERR_INVALID_ARG),
     (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG),
-    (dict(causal=0), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(causal=0), bnd.ATF_ERR_WORKSPACE),           # valid (non-causal): stops at the workspace
     (dict(causal=2), bnd.ATF_ERR_INVALID_ARG),
     (dict(dtype=7), bnd.ATF_ERR_INVALID_ARG),
     (dict(pos0=-1), bnd.ATF_ERR_INVALID_ARG),
@@ -263,7 +278,7 @@ def _call_pdecode(lib, **kw):
     (dict(sl=258), bnd.ATF_ERR_INVALID_ARG), (dict(max_len=257), bnd.ATF_ERR_INVALID_ARG),
     (dict(max_len=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
     (dict(Hq=5), bnd.ATF_ERR_INVALID_ARG), (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
-    (dict(causal=0), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(causal=0), bnd.ATF_ERR_WORKSPACE),           # valid (non-causal): stops at the workspace (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
     (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG), (dict(ws_bytes=1), bnd.ATF_ERR_WORKSPACE),
 ])
 def test_paged_decode_rejects(lib, kw, expect):
