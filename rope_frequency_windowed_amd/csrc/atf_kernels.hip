@@ -362,6 +362,44 @@ __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, 
 #undef ATF_CHAIN
 }
 
+// Both score chains of a pair of blocks that share one pair cut (first kept
+// K-step S0) and the first block's probabilities: one straight-line run per
+// S0.  The exponentials depend on the first chain and the run ends with the
+// second, so they stay inside the run, beside the second chain's MFMAs.
+template <int NSTEP, int S0>
+__device__ __attribute__((always_inline)) inline void qk_pair_chain(
+    const unsigned char *lds, unsigned kb0, unsigned kb1, unsigned ky, const bf16x8_t *qf, int zero_below,
+    bf16x8_t ones_a, bf16x8_t negm_b, f32x16_t &s0, f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
+    s0 = qk_chain<NSTEP, S0>(lds, kb0, ky, qf, zero_below, ones_a, negm_b);
+    block_probs(s0, pw, lsum);
+    s1 = qk_chain<NSTEP, S0>(lds, kb1, ky, qf, zero_below, ones_a, negm_b);
+}
+
+template <int NSTEP>
+__device__ inline void qk_pair(int s_first, const unsigned char *lds, unsigned kb0, unsigned kb1, unsigned ky,
+                               const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b, f32x16_t &s0,
+                               f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
+#define ATF_PAIR(s0_) \
+    qk_pair_chain<NSTEP, s0_>(lds, kb0, kb1, ky, qf, zero_below, ones_a, negm_b, s0, s1, pw, lsum)
+    switch (s_first) {
+        case 0: ATF_PAIR(0); return;
+        case 1: ATF_PAIR(1); return;
+        case 2: ATF_PAIR(2); return;
+        default: break;
+    }
+    if constexpr (NSTEP > 4) {
+        switch (s_first) {
+            case 3: ATF_PAIR(3); return;
+            case 4: ATF_PAIR(4); return;
+            case 5: ATF_PAIR(5); return;
+            case 6: ATF_PAIR(6); return;
+            default: ATF_PAIR((NSTEP > 4 ? 7 : 3)); return;
+        }
+    }
+    ATF_PAIR(NSTEP - 1);
+#undef ATF_PAIR
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill_bf16_kernel(AttnArgs a) {
     constexpr int P = D / 2;
@@ -498,6 +536,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     // dropped-term count: per lane where it differs between lanes, uniform
     // (whole-block) contributions in skipped_u
     unsigned long long skipped = 0, skipped_u = 0;
+    unsigned fast_cut = 0;  // sum of the pair cut over fast tiles (x NB x 16 x n_valid at the end)
     const unsigned n_valid = (unsigned)__builtin_popcountll(__ballot(q_valid));
     const f32x16_t zero16 = {};
     const int koff0 = 4 * half;
@@ -525,6 +564,78 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
         f32x16_t sacc[2];
         unsigned pw[2][8];
         float lsum[2];
+
+        // Move the reference when block kb's probabilities overflow kSumLimit
+        // (or at the first block): block max becomes the reference, O and l are
+        // rescaled, the block's probabilities are redone; the next block, already
+        // scored against the old reference (when `later` holds), is shifted too.
+#define ATF_BLOCK_RESCALE(sl, later)                                                              \
+        if (__ballot(first || !(lsum[sl] <= kSumLimit))) {                                        \
+            float bm = sacc[sl][0];                                                               \
+            _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[sl][r]);           \
+            bm = partner_max(bm);                                                                 \
+            const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm)); \
+            const float shift = m_new - m_ref;                                                    \
+            if (!first) {                                                                         \
+                const float corr = fast_exp2(-shift);                                             \
+                l_run *= corr;                                                                    \
+                _Pragma("unroll") for (int db = 0; db < NDB; ++db)                                \
+                    _Pragma("unroll") for (int r = 0; r < 16; ++r) o[db][r] *= corr;              \
+            }                                                                                     \
+            m_ref = m_new;                                                                        \
+            if (later) {                                                                          \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[(sl) ^ 1][r] -= shift;        \
+            }                                                                                     \
+            negm_b = __builtin_bit_cast(bf16x8_t,                                                 \
+                                        (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u}); \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[sl][r] -= shift;                  \
+            block_probs(sacc[sl], pw[sl], lsum[sl]);                                              \
+        }                                                                                         \
+        first = false;                                                                            \
+        l_run += lsum[sl];
+
+        // Fast tile (the common case, causal): for this wave every key of the
+        // tile precedes every query and no window W_p falls inside the tile's
+        // distance range, so all its blocks keep the same pair suffix [p_t, P)
+        // with no per-element work.
+        bool fast;
+        int p_t;
+        {
+            const int jl = j0 + KT - 1;
+            int dmin, dmax;
+            if (CAUSAL) {
+                fast = jl <= i0k;
+                dmin = i0k - jl;
+                dmax = i0k + 31 - j0;
+            } else {
+                // (the non-causal kernel keeps the general path: its extra
+                // masks leave no registers for a second copy of the tile body)
+                fast = false;
+                dmin = dmax = 0;
+            }
+            const int plo_t = __builtin_popcountll(__ballot(w_lane < dmin));
+            p_t = __builtin_popcountll(__ballot(w_lane < dmax));
+            fast = fast && plo_t == p_t;
+        }
+        if (CAUSAL && fast) {
+            fast_cut += (unsigned)p_t;
+            const int sf = p_t >> 3, zb = p_t - 8 * sf - koff0;
+#pragma unroll
+            for (int kp = 0; kp < NB; kp += 2) {
+                const unsigned char *lv = lt + (kp >> 1) * (D * 128);
+                qk_pair<NSTEP>(sf, lt, kbase_lane + 32u * kp * (CH * 16), kbase_lane + 32u * (kp + 1) * (CH * 16), ky,
+                               qf, zb, ones_a, negm_b, sacc[0], sacc[1], pw[0], lsum[0]);
+                ATF_BLOCK_RESCALE(0, true)
+                block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
+                block_probs(sacc[1], pw[1], lsum[1]);
+                ATF_BLOCK_RESCALE(1, false)
+                block_pv<NDB>(o, lv, vbase_lane, vz, 1, pw[1]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the next tile
+            __syncthreads();
+            continue;
+        }
+
         int p_lo[NB], p_full[NB];
         bool live[NB];
 #pragma unroll
@@ -593,34 +704,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             }                                                                                     \
         }
 
-        // Move the reference when block kb's probabilities overflow kSumLimit
-        // (or at the first block): block max becomes the reference, O and l are
-        // rescaled, the block's probabilities are redone; the next block, already
-        // scored against the old reference (when `later` holds), is shifted too.
-#define ATF_BLOCK_RESCALE(sl, later)                                                              \
-        if (__ballot(first || !(lsum[sl] <= kSumLimit))) {                                        \
-            float bm = sacc[sl][0];                                                               \
-            _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[sl][r]);           \
-            bm = partner_max(bm);                                                                 \
-            const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm)); \
-            const float shift = m_new - m_ref;                                                    \
-            if (!first) {                                                                         \
-                const float corr = fast_exp2(-shift);                                             \
-                l_run *= corr;                                                                    \
-                _Pragma("unroll") for (int db = 0; db < NDB; ++db)                                \
-                    _Pragma("unroll") for (int r = 0; r < 16; ++r) o[db][r] *= corr;              \
-            }                                                                                     \
-            m_ref = m_new;                                                                        \
-            if (later) {                                                                          \
-                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[(sl) ^ 1][r] -= shift;        \
-            }                                                                                     \
-            negm_b = __builtin_bit_cast(bf16x8_t,                                                 \
-                                        (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u}); \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[sl][r] -= shift;                  \
-            block_probs(sacc[sl], pw[sl], lsum[sl]);                                              \
-        }                                                                                         \
-        first = false;                                                                            \
-        l_run += lsum[sl];
 
 #pragma unroll
         for (int kp = 0; kp < NB; kp += 2) {  // pairs of blocks: slot 0 = block kp, slot 1 = kp + 1
@@ -672,6 +755,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                 *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
             }
     }
+    skipped_u += (unsigned long long)fast_cut * (NB * 16u) * n_valid;
     skipped = wave_sum_u64(skipped) + skipped_u;
     if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
 }
