@@ -31,6 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "atf_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 W_INF = np.iinfo(np.int64).max
+LAYOUTS = {"neox": 0, "gptj": 1}
 
 _lib = None
 
@@ -56,7 +57,7 @@ def _bind(path: str):
     lib.orc_window_table.restype = ctypes.c_int
     lib.orc_attention_rows.argtypes = [
         f32p, f32p, f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
         ctypes.c_int, ctypes.c_int64, ctypes.c_int64, i64p, ctypes.c_int64, f32p, f64p, u64p]
     lib.orc_attention_rows.restype = ctypes.c_int
     lib.orc_skipped_closed_form.argtypes = [
@@ -109,7 +110,7 @@ class Oracle:
         return np.ascontiguousarray(x, dtype=np.float32)
 
     def attention(self, q, k, v, *, base: float, alpha: float, causal: bool = True,
-                  q_pos0: int = 0, k_pos0: int = 0, rows=None, q_shape=None):
+                  q_pos0: int = 0, k_pos0: int = 0, rows=None, q_shape=None, layout: str = "neox"):
         """Windowed-RoPE attention in fp64.
 
         q: [B, Hq, Sq, d]; k, v: [B, Hkv, Sk, d] (any float dtype; values are used
@@ -117,9 +118,13 @@ class Oracle:
         ``rows``: optional int array [n, 3] of (b, h_q, i); default all rows.
         ``q_shape``: if given as (B, Hq, Sq, d), ``q`` holds only the listed
         rows' query vectors, [n, d] (for sampled rows of huge inputs).
+        ``layout``: "neox" (pair p = dims p and p + d/2) or "gptj" (pair p =
+        dims 2p and 2p + 1).
         Returns (out, skipped): out is [n, d] fp64 when ``rows`` is given, else
         [B, Hq, Sq, d]; skipped is the number of dropped (row, key, pair) terms.
         """
+        if layout not in LAYOUTS:
+            raise ValueError("layout must be one of %s" % sorted(LAYOUTS))
         q32, k32, v32 = self._as_f32(q), self._as_f32(k), self._as_f32(v)
         compact = q_shape is not None
         if compact and rows is None:
@@ -141,7 +146,7 @@ class Oracle:
         rc = self.lib.orc_attention_rows(
             None if compact else q32.ctypes.data_as(f32p), k32.ctypes.data_as(f32p),
             v32.ctypes.data_as(f32p),
-            B, Hq, Hkv, Sq, Sk, d, float(base), float(alpha), 1 if causal else 0,
+            B, Hq, Hkv, Sq, Sk, d, LAYOUTS[layout], float(base), float(alpha), 1 if causal else 0,
             int(q_pos0), int(k_pos0),
             rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.shape[0],
             q32.ctypes.data_as(f32p) if compact else None,

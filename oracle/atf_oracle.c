@@ -24,10 +24,12 @@
  *              ("proportional distance"; the slowest pair is never cut, which
  *              is what keeps every causal key reachable); alpha = +inf turns
  *              every window off.
- *   pair p   = dims (p, p + P) (NeoX half-split layout)
- *   rotation by +angle: x'_p = x_p cos a - x_{p+P} sin a,
- *                       x'_{p+P} = x_{p+P} cos a + x_p sin a, a = pos*theta_p
- *   pair p contributes q'_p k'_p + q'_{p+P} k'_{p+P} to score(i,j) iff
+ *   pair p   = dims (lo, hi) = (p, p + P) in the NeoX half-split layout
+ *              (layout 0), or (2p, 2p + 1) in the GPT-J interleaved layout
+ *              (layout 1); the frequency theta_p is the same in both
+ *   rotation by +angle: x'_lo = x_lo cos a - x_hi sin a,
+ *                       x'_hi = x_hi cos a + x_lo sin a, a = pos*theta_p
+ *   pair p contributes q'_lo k'_lo + q'_hi k'_hi to score(i,j) iff
  *   delta = pos_q - pos_k <= W_p (|delta| when not causal); dropped terms
  *   add 0 (they are not -inf); logits = score / sqrt(d).
  *
@@ -75,18 +77,23 @@ static int orc_kept(int64_t delta, int causal, int64_t Wp)
     return Wp == ORC_W_INF || dist <= Wp;
 }
 
+/* The two dims of pair p: (p, p + P) half-split, (2p, 2p + 1) interleaved. */
+static int orc_dim_lo(int p, int P, int layout) { return layout ? 2 * p : p; }
+static int orc_dim_hi(int p, int P, int layout) { return layout ? 2 * p + 1 : p + P; }
+
 /* Rotate one row x[0..d) at position pos into y (fp64). */
-static void orc_rotate(const float *x, int d, double pos, const double *theta, double *y)
+static void orc_rotate(const float *x, int d, int layout, double pos, const double *theta, double *y)
 {
     const int P = d / 2;
     for (int p = 0; p < P; ++p) {
+        const int il = orc_dim_lo(p, P, layout), ih = orc_dim_hi(p, P, layout);
         double a = pos * theta[p];
         double c = cos(a);
         double s = sin(a);
-        double lo = (double)x[p];
-        double hi = (double)x[p + P];
-        y[p] = lo * c - hi * s;
-        y[p + P] = hi * c + lo * s;
+        double lo = (double)x[il];
+        double hi = (double)x[ih];
+        y[il] = lo * c - hi * s;
+        y[ih] = hi * c + lo * s;
     }
 }
 
@@ -101,12 +108,13 @@ static void orc_rotate(const float *x, int d, double pos, const double *theta, d
  *       instead of q[b][h_q][i] (lets a caller pass only sampled rows);
  *       q may then be NULL.
  *   GQA: query head h reads key/value head h / (Hq / Hkv).
+ *   layout: 0 = NeoX half-split pairs, 1 = GPT-J interleaved pairs.
  *   skipped (nullable): number of (row, key, pair) terms left out, summed
  *   over the listed rows (causal keys only when causal != 0).
  * Returns 0, or -1 on bad arguments.
  */
 int orc_attention_rows(const float *q, const float *k, const float *v,
-                       int B, int Hq, int Hkv, int64_t Sq, int64_t Sk, int d,
+                       int B, int Hq, int Hkv, int64_t Sq, int64_t Sk, int d, int layout,
                        double base, double alpha, int causal,
                        int64_t q_pos0, int64_t k_pos0,
                        const int64_t *rows, int64_t n_rows, const float *q_rows,
@@ -115,6 +123,8 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || (Hq % Hkv) != 0 || Sq <= 0 || Sk <= 0)
         return -1;
     if (d <= 0 || (d % 2) != 0 || rows == NULL || out == NULL || n_rows < 0)
+        return -1;
+    if (layout != 0 && layout != 1)
         return -1;
     if (q == NULL && q_rows == NULL)
         return -1;
@@ -162,7 +172,7 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
 
 #pragma omp parallel for schedule(static)
             for (int64_t j = 0; j < Sk; ++j)
-                orc_rotate(kh + (size_t)j * d, d, (double)(k_pos0 + j), theta,
+                orc_rotate(kh + (size_t)j * d, d, layout, (double)(k_pos0 + j), theta,
                            krot + (size_t)j * d);
 
             uint64_t skipped_here = 0;
@@ -179,7 +189,7 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
                     const float *qrow = q_rows ? q_rows + (size_t)r * d
                                                : q + (((size_t)b * Hq + h) * (size_t)Sq + i) * d;
                     int64_t qpos = q_pos0 + i;
-                    orc_rotate(qrow, d, (double)qpos, theta, qrot);
+                    orc_rotate(qrow, d, layout, (double)qpos, theta, qrot);
 
                     /* pass 1: windowed scores and their maximum */
                     double m = -INFINITY;
@@ -193,7 +203,8 @@ int orc_attention_rows(const float *q, const float *k, const float *v,
                         double s = 0.0;
                         for (int p = 0; p < P; ++p) {
                             if (orc_kept(delta, causal, W[p])) {
-                                double term = qrot[p] * kr[p] + qrot[p + P] * kr[p + P];
+                                const int il = orc_dim_lo(p, P, layout), ih = orc_dim_hi(p, P, layout);
+                                double term = qrot[il] * kr[il] + qrot[ih] * kr[ih];
                                 s += term;
                             } else {
                                 skipped_here += 1;

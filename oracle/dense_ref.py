@@ -29,9 +29,24 @@ def rope_half_split(x: np.ndarray, positions: np.ndarray, base: float) -> np.nda
     return x * cos + rot_half * sin
 
 
+def rope_interleaved(x: np.ndarray, positions: np.ndarray, base: float) -> np.ndarray:
+    """GPT-J rotary: dims (2p, 2p+1) read as the complex number x_2p + i x_2p+1,
+    multiplied by exp(i * position * base^(-2p/d)), written back interleaved."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    inv_freq = base ** (-np.arange(d // 2, dtype=np.float64) * 2.0 / d)
+    z = z * np.exp(1j * np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :])
+    out = np.empty_like(x)
+    out[..., 0::2] = z.real
+    out[..., 1::2] = z.imag
+    return out
+
+
 def dense_rope_attention(q, k, v, *, base: float, causal: bool = True,
-                         q_pos0: int = 0, k_pos0: int = 0) -> np.ndarray:
-    """q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] -> out [B,Hq,Sq,d] in fp64."""
+                         q_pos0: int = 0, k_pos0: int = 0, layout: str = "neox") -> np.ndarray:
+    """q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] -> out [B,Hq,Sq,d] in fp64.
+    layout "neox": rotate_half rotary; "gptj": interleaved (complex) rotary."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -40,8 +55,9 @@ def dense_rope_attention(q, k, v, *, base: float, causal: bool = True,
     group = Hq // Hkv
     qpos = q_pos0 + np.arange(Sq)
     kpos = k_pos0 + np.arange(Sk)
-    qr = rope_half_split(q, qpos, base)
-    kr = rope_half_split(k, kpos, base)
+    rope = rope_interleaved if layout == "gptj" else rope_half_split
+    qr = rope(q, qpos, base)
+    kr = rope(k, kpos, base)
     kr = np.repeat(kr, group, axis=1)
     vv = np.repeat(v, group, axis=1)
     logits = qr @ np.swapaxes(kr, -1, -2) / np.sqrt(d)

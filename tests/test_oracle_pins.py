@@ -244,6 +244,74 @@ def test_single_pair_decode_geometry(orc):
     assert skipped == orc.skipped_closed_form(S, d, base, alpha, decode=True)
 
 
+# ------------------------------------------------------ GPT-J interleaved pairs
+
+def halfsplit_of_interleaved(x):
+    """Dims (2p, 2p+1) of each row moved to (p, p+P): the half-split row that
+    carries the same rotary pairs."""
+    x = np.asarray(x)
+    return np.concatenate([x[..., 0::2], x[..., 1::2]], axis=-1)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gptj_alpha_inf_equals_dense(orc, causal):
+    """Windows off: the interleaved layout equals dense attention whose rotary
+    is the complex-number rotation of (x_2p + i x_2p+1)."""
+    B, Hq, Hkv, S, d = 1, 4, 2, 75, 32
+    q, k, v = rnd((B, Hq, S, d), 151), rnd((B, Hkv, S, d), 152), rnd((B, Hkv, S, d), 153)
+    out, skipped = orc.attention(q, k, v, base=1e4, alpha=math.inf, causal=causal, q_pos0=7, k_pos0=7,
+                                 layout="gptj")
+    ref = dense_ref.dense_rope_attention(q, k, v, base=1e4, causal=causal, q_pos0=7, k_pos0=7, layout="gptj")
+    assert skipped == 0
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("alpha", [0.3, 1.0])
+def test_gptj_equals_halfsplit_on_moved_dims(orc, alpha):
+    """Pair p is the same pair in both layouts, only stored elsewhere: moving
+    q's and k's dims (2p, 2p+1) to (p, p+P) gives the half-split result
+    exactly, windows and count included (values are not rotary, not moved)."""
+    B, Hq, Hkv, S, d = 2, 4, 2, 140, 32
+    q, k, v = rnd((B, Hq, S, d), 161), rnd((B, Hkv, S, d), 162), rnd((B, Hkv, S, d), 163)
+    a, sa = orc.attention(q, k, v, base=50.0, alpha=alpha, layout="gptj")
+    b, sb = orc.attention(halfsplit_of_interleaved(q), halfsplit_of_interleaved(k), v, base=50.0, alpha=alpha)
+    assert sa == sb > 0
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("p", [0, 5, 15])
+def test_gptj_single_pair_explicit_logits(orc, p):
+    """q, k on dims (2p, 2p+1) only: the relative-angle formula with a cut
+    window, written for that pair."""
+    S, d, base, alpha = 240, 32, 20.0, 0.8
+    q, k, v = rnd((1, 1, S, d), 170 + p), rnd((1, 1, S, d), 180 + p), rnd((1, 1, S, d), 190 + p)
+    mask = np.zeros(d, dtype=np.float32)
+    mask[[2 * p, 2 * p + 1]] = 1.0
+    q, k = q * mask, k * mask
+    W = orc.window_table(d, base, alpha)
+    out, _ = orc.attention(q, k, v, base=base, alpha=alpha, q_pos0=4, k_pos0=4, layout="gptj")
+    pos = 4 + np.arange(S)
+    Wp = np.inf if W[p] == orc.W_INF else float(W[p])
+    ref = explicit_single_pair(halfsplit_of_interleaved(q[0, 0]), halfsplit_of_interleaved(k[0, 0]), v[0, 0], p,
+                               base, Wp, pos, pos)
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-11, rtol=0)
+
+
+def test_gptj_shift_invariance(orc):
+    B, Hq, Hkv, S, d = 1, 2, 1, 100, 64
+    q, k, v = rnd((B, Hq, S, d), 201), rnd((B, Hkv, S, d), 202), rnd((B, Hkv, S, d), 203)
+    a, sa = orc.attention(q, k, v, base=1e4, alpha=1.0, layout="gptj")
+    b, sb = orc.attention(q, k, v, base=1e4, alpha=1.0, q_pos0=2 ** 22, k_pos0=2 ** 22, layout="gptj")
+    assert sa == sb
+    np.testing.assert_allclose(a, b, atol=1e-9, rtol=0)
+
+
+def test_layout_name_checked(orc):
+    q = rnd((1, 1, 4, 8), 1)
+    with pytest.raises(ValueError):
+        orc.attention(q, q, q, base=1e4, alpha=1.0, layout="interleaved")
+
+
 # ------------------------------------------------------------------ invariances
 
 @pytest.mark.parametrize("shift", [2 ** 20, 2 ** 24 + 3])

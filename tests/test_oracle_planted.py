@@ -30,6 +30,8 @@ def _checks(o):
         "gqa": lambda: pins.test_gqa_equals_repeated_heads(o),
         "reachable": lambda: pins.test_every_causal_key_reachable(o),
         "slowest": lambda: pins.test_slowest_pair_only_equals_dense(o, 1.0),
+        "gptj_dense": lambda: pins.test_gptj_alpha_inf_equals_dense(o, True),
+        "gptj_moved": lambda: pins.test_gptj_equals_halfsplit_on_moved_dims(o, 1.0),
     }
     failed = []
     for name, fn in cases.items():
@@ -41,9 +43,15 @@ def _checks(o):
 
 
 MUTATIONS = {
-    "rotation_sign": ("y[p] = lo * c - hi * s;", "y[p] = lo * c + hi * s;"),
-    "dropped_hi_term": ("double term = qrot[p] * kr[p] + qrot[p + P] * kr[p + P];",
-                        "double term = qrot[p] * kr[p];"),
+    "rotation_sign": ("y[il] = lo * c - hi * s;", "y[il] = lo * c + hi * s;"),
+    "dropped_hi_term": ("double term = qrot[il] * kr[il] + qrot[ih] * kr[ih];",
+                        "double term = qrot[il] * kr[il];"),
+    "gptj_dims_swapped": ("{ return layout ? 2 * p : p; }\nstatic int orc_dim_hi(int p, int P, int layout) "
+                          "{ return layout ? 2 * p + 1 : p + P; }",
+                          "{ return layout ? 2 * p + 1 : p; }\nstatic int orc_dim_hi(int p, int P, int layout) "
+                          "{ return layout ? 2 * p : p + P; }"),
+    "gptj_layout_ignored_lo": ("static int orc_dim_lo(int p, int P, int layout) { return layout ? 2 * p : p; }",
+                               "static int orc_dim_lo(int p, int P, int layout) { return p; }"),
     "window_exclusive": ("return Wp == ORC_W_INF || dist <= Wp;", "return Wp == ORC_W_INF || dist < Wp;"),
     "window_floor": ("double w = ceil(alpha * lambda);", "double w = floor(alpha * lambda);"),
     "last_pair_cut": ("if (p == P - 1 || isinf(alpha)) {", "if (isinf(alpha)) {"),
