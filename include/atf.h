@@ -11,7 +11,10 @@
  *   Section "Die Zahlen - und ihre Grenze": prefill and decode attention keep
  *   their online-softmax recurrence unchanged.
  *   Readings used where the page gives no formula:
- *     P = d/2 pairs, pair p = head dims (p, p + P) (half-split layout),
+ *     P = d/2 pairs; pair p = head dims (p, p + P) in the half-split (NeoX)
+ *     layout, or (2p, 2p + 1) in the interleaved (GPT-J) layout -- the
+ *     formulas below write the half-split dims; the interleaved layout uses
+ *     the same theta_p, W_p and rotation on its own pair of dims,
  *     theta_p = rope_base^(-2p/d), lambda_p = 2*pi/theta_p,
  *     W_p = ceil(alpha * lambda_p) for p < P-1, W_{P-1} = infinity,
  *     rotation by +angle (pos * theta_p):
@@ -38,6 +41,8 @@
  *   - Supported: d in {64, 128}; Hq % Hkv == 0; Hq/Hkv <= 64; S >= 1;
  *     0 <= pos0 and pos0 + S + 1 < 2^31; alpha > 0 (finite or +inf; +inf
  *     means no window); rope_base > 1 and finite; causal in {0, 1}.
+ *   - rope_layout (calls that read q or k rows): ATF_ROPE_NEOX or
+ *     ATF_ROPE_GPTJ, the same for q and k (see atf_rope_layout).
  *   - causal = 1: query i sees the keys at or before its position.  causal = 0
  *     (prefill): every key, the windows applying to the distance |i - j| (no
  *     page fixes the non-causal case; it is the plain reading of a distance
@@ -64,6 +69,16 @@ typedef enum {
 } atf_status;
 
 typedef enum { ATF_F32 = 0, ATF_BF16 = 1 } atf_dtype;
+
+/* How a head's d dims form the rotary pairs (argument `rope_layout`, int32_t).
+ * The pages treat a pair as the unit a window cuts without fixing where its
+ * two dims are stored; both common layouts are accepted.  Any other value is
+ * ATF_ERR_INVALID_ARG.  In the interleaved layout a key's kept pairs are one
+ * contiguous suffix of its row. */
+typedef enum {
+    ATF_ROPE_NEOX = 0, /* pair p = dims (p, p + d/2)  (rotate-half) */
+    ATF_ROPE_GPTJ = 1  /* pair p = dims (2p, 2p + 1)  (interleaved) */
+} atf_rope_layout;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *atf_status_string(atf_status s);
@@ -104,7 +119,7 @@ size_t atf_prefill_workspace_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d,
  */
 atf_status atf_prefill(const void *q, const void *k, const void *v, void *out,
                        int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
-                       double rope_base, double alpha, int32_t causal, int64_t pos0,
+                       int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                        atf_dtype dtype, void *workspace, size_t workspace_bytes,
                        uint64_t *skipped_out, atf_stream_t stream);
 
@@ -117,7 +132,7 @@ atf_status atf_prefill(const void *q, const void *k, const void *v, void *out,
  */
 atf_status atf_prefill_prepare_kv(const void *k, const void *v,
                                   int32_t B, int32_t Hkv, int64_t S, int32_t d,
-                                  double rope_base, int64_t pos0, atf_dtype dtype,
+                                  int32_t rope_layout, double rope_base, int64_t pos0, atf_dtype dtype,
                                   void *workspace, size_t workspace_bytes, atf_stream_t stream);
 
 /*
@@ -128,7 +143,7 @@ atf_status atf_prefill_prepare_kv(const void *k, const void *v,
  */
 atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void *out,
                               int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
-                              double rope_base, double alpha, int32_t causal, int64_t pos0,
+                              int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                               atf_dtype dtype, void *workspace, size_t workspace_bytes,
                               uint64_t *skipped_out, atf_stream_t stream);
 
@@ -149,7 +164,7 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
  */
 atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *out,
                              int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d,
-                             double rope_base, double alpha, int32_t causal, int64_t pos0,
+                             int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                              atf_dtype dtype, void *workspace, size_t workspace_bytes,
                              uint64_t *skipped_out, atf_stream_t stream);
 
@@ -168,7 +183,7 @@ size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
  */
 atf_status atf_decode(const void *q, const void *k, const void *v, void *out,
                       int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
-                      double rope_base, double alpha, int32_t causal, int64_t pos0,
+                      int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                       atf_dtype dtype, void *workspace, size_t workspace_bytes,
                       uint64_t *skipped_out, atf_stream_t stream);
 
@@ -203,7 +218,7 @@ size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d);
  * on `stream`.
  */
 atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n,
-                             int64_t k_begin, int64_t cap, int32_t d, double rope_base,
+                             int64_t k_begin, int64_t cap, int32_t d, int32_t rope_layout, double rope_base,
                              int64_t pos0, atf_dtype dtype, atf_stream_t stream);
 
 /*
@@ -217,7 +232,7 @@ atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv
  */
 atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, void *out,
                              int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int64_t cap, int32_t d,
-                             double rope_base, double alpha, int32_t causal, int64_t pos0,
+                             int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                              atf_dtype dtype, void *workspace, size_t workspace_bytes,
                              uint64_t *skipped_out, atf_stream_t stream);
 
@@ -258,7 +273,7 @@ size_t atf_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int6
 atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpool,
                            const int32_t *page_table, int32_t max_pages, int32_t num_pages,
                            int32_t B, int32_t Hkv, int64_t n, int64_t k_begin, int32_t d,
-                           double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream);
+                           int32_t rope_layout, double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream);
 
 /*
  * Ragged decode over the paged cache: sequence b's query q[b] ([B][Hq][1][d])
@@ -275,7 +290,7 @@ atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpoo
 atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool, void *out,
                             const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
                             int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len,
-                            int32_t d, double rope_base, double alpha, int32_t causal, int64_t pos0,
+                            int32_t d, int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
                             atf_dtype dtype, void *workspace, size_t workspace_bytes,
                             uint64_t *skipped_out, atf_stream_t stream);
 

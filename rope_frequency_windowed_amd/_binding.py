@@ -61,37 +61,39 @@ def _lib():
     lib.atf_skipped_pair_products.restype = ctypes.c_int
     lib.atf_prefill_workspace_bytes.argtypes = [i32, i32, i64, i32, ctypes.c_int]
     lib.atf_prefill_workspace_bytes.restype = sz
-    lib.atf_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+    lib.atf_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f64, f64, i32, i64,
                                 ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill.restype = ctypes.c_int
-    lib.atf_prefill_prepare_kv.argtypes = [vp, vp, i32, i32, i64, i32, f64, i64, ctypes.c_int,
+    lib.atf_prefill_prepare_kv.argtypes = [vp, vp, i32, i32, i64, i32, i32, f64, i64, ctypes.c_int,
                                            vp, sz, vp]
     lib.atf_prefill_prepare_kv.restype = ctypes.c_int
-    lib.atf_prefill_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+    lib.atf_prefill_attend.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f64, f64, i32, i64,
                                        ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill_attend.restype = ctypes.c_int
-    lib.atf_prefill_chunk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, f64, f64, i32, i64,
+    lib.atf_prefill_chunk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f64, f64, i32, i64,
                                       ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill_chunk.restype = ctypes.c_int
     lib.atf_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
     lib.atf_decode_workspace_bytes.restype = sz
-    lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+    lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f64, f64, i32, i64,
                                ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode.restype = ctypes.c_int
     lib.atf_decode_kcache_bytes.argtypes = [i32, i32, i64, i32]
     lib.atf_decode_kcache_bytes.restype = sz
-    lib.atf_decode_pack_k.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, f64, i64, ctypes.c_int, vp]
+    lib.atf_decode_pack_k.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, i32, f64, i64, ctypes.c_int, vp]
     lib.atf_decode_pack_k.restype = ctypes.c_int
-    lib.atf_decode_kcache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, f64, f64, i32, i64,
+    lib.atf_decode_kcache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f64, f64, i32, i64,
                                       ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode_kcache.restype = ctypes.c_int
     lib.atf_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
     lib.atf_decode_paged_workspace_bytes.restype = sz
     lib.atf_paged_page_bytes.argtypes = [i32, i32]
     lib.atf_paged_page_bytes.restype = sz
-    lib.atf_paged_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32, f64, i64, ctypes.c_int, vp]
+    lib.atf_paged_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i64, i32, i32, f64, i64, ctypes.c_int,
+                                    vp]
     lib.atf_paged_write.restype = ctypes.c_int
-    lib.atf_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, f64, f64, i32, i64,
+    lib.atf_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, f64, f64, i32,
+                                     i64,
                                      ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode_paged.restype = ctypes.c_int
     _LIB = lib
@@ -180,8 +182,21 @@ def workspace(nbytes: int, device, tag: str):
     return ws
 
 
+ROPE_LAYOUTS = {"neox": 0, "gptj": 1}
+
+
+def _layout_code(rope_layout) -> int:
+    """"neox" (pair p = dims p, p + d/2) -> 0, "gptj" (dims 2p, 2p + 1) -> 1;
+    an int is passed through unchanged (the library checks it)."""
+    if isinstance(rope_layout, str):
+        if rope_layout not in ROPE_LAYOUTS:
+            raise ValueError("rope_layout must be one of %s" % sorted(ROPE_LAYOUTS))
+        return ROPE_LAYOUTS[rope_layout]
+    return int(rope_layout)
+
+
 def atf_prefill(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
-                ws=None, return_skipped: bool = False):
+                ws=None, return_skipped: bool = False, rope_layout="neox"):
     """Causal windowed-RoPE prefill.  q [B,Hq,S,d], k/v [B,Hkv,S,d] (pre-RoPE)."""
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
@@ -193,31 +208,32 @@ def atf_prefill(q, k, v, out=None, *, rope_base: float, alpha: float, causal: in
         ws = workspace(nbytes, q.device, "prefill")
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                              B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal), int(pos0),
+                              B, Hq, Hkv, S, d, _layout_code(rope_layout), float(rope_base), float(alpha), int(causal), int(pos0),
                               code, _dev(ws, "workspace"), ws.numel(),
                               ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_prefill")
     return (out, int(skipped.value)) if return_skipped else out
 
 
-def atf_prefill_prepare_kv(k, v, *, rope_base: float, pos0: int = 0, ws):
+def atf_prefill_prepare_kv(k, v, *, rope_base: float, pos0: int = 0, ws, rope_layout="neox"):
     B, Hkv, S, d = k.shape
     code = _dtype_code(k)
-    _check(_lib().atf_prefill_prepare_kv(_dev(k, "k"), _dev(v, "v"), B, Hkv, S, d, float(rope_base),
+    _check(_lib().atf_prefill_prepare_kv(_dev(k, "k"), _dev(v, "v"), B, Hkv, S, d, _layout_code(rope_layout),
+                                         float(rope_base),
                                          int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                          _stream(k.device)),
            "atf_prefill_prepare_kv")
 
 
 def atf_prefill_attend(q, k, v, out, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
-                       ws, return_skipped: bool = False):
+                       ws, return_skipped: bool = False, rope_layout="neox"):
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     code = _dtype_code(q)
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_prefill_attend(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                     B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal),
-                                     int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                     B, Hq, Hkv, S, d, _layout_code(rope_layout), float(rope_base), float(alpha),
+                                     int(causal), int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                      ctypes.byref(skipped) if return_skipped else None,
                                      _stream(q.device)),
            "atf_prefill_attend")
@@ -225,7 +241,7 @@ def atf_prefill_attend(q, k, v, out, *, rope_base: float, alpha: float, causal: 
 
 
 def atf_prefill_chunk(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
-                      ws=None, return_skipped: bool = False):
+                      ws=None, return_skipped: bool = False, rope_layout="neox"):
     """Chunked prefill: q [B,Hq,Sq,d] are the last Sq of the Sk tokens whose
     keys/values k, v [B,Hkv,Sk,d] hold (pre-RoPE); query i sits at pos0+Sk-Sq+i."""
     B, Hq, Sq, d = q.shape
@@ -238,15 +254,15 @@ def atf_prefill_chunk(q, k, v, out=None, *, rope_base: float, alpha: float, caus
         ws = workspace(nbytes, q.device, "prefill")
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_prefill_chunk(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                                    B, Hq, Hkv, Sq, Sk, d, float(rope_base), float(alpha), int(causal),
-                                    int(pos0), code, _dev(ws, "workspace"), ws.numel(),
+                                    B, Hq, Hkv, Sq, Sk, d, _layout_code(rope_layout), float(rope_base),
+                                    float(alpha), int(causal), int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                     ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_prefill_chunk")
     return (out, int(skipped.value)) if return_skipped else out
 
 
 def atf_decode(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int = 1, pos0: int = 0,
-               ws=None, return_skipped: bool = False):
+               ws=None, return_skipped: bool = False, rope_layout="neox"):
     """Windowed-RoPE decode: q [B,Hq,1,d] at position pos0+S over the cache k/v [B,Hkv,S,d]."""
     B, Hq, one, d = q.shape
     if one != 1:
@@ -260,7 +276,7 @@ def atf_decode(q, k, v, out=None, *, rope_base: float, alpha: float, causal: int
         ws = workspace(nbytes, q.device, "decode")
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_decode(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"),
-                             B, Hq, Hkv, S, d, float(rope_base), float(alpha), int(causal), int(pos0),
+                             B, Hq, Hkv, S, d, _layout_code(rope_layout), float(rope_base), float(alpha), int(causal), int(pos0),
                              code, _dev(ws, "workspace"), ws.numel(),
                              ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode")
@@ -271,16 +287,16 @@ def atf_decode_kcache_bytes(B: int, Hkv: int, cap: int, d: int) -> int:
     return int(_lib().atf_decode_kcache_bytes(B, Hkv, cap, d))
 
 
-def atf_decode_pack_k(k, kcache, *, k_begin: int, cap: int, rope_base: float, pos0: int = 0):
+def atf_decode_pack_k(k, kcache, *, k_begin: int, cap: int, rope_base: float, pos0: int = 0, rope_layout="neox"):
     """Write k [B,Hkv,n,d] (pre-RoPE, bf16) as cache keys k_begin.. of kcache."""
     B, Hkv, n, d = k.shape
     _check(_lib().atf_decode_pack_k(_dev(k, "k"), _dev(kcache, "kcache"), B, Hkv, n, int(k_begin), int(cap), d,
-                                    float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
+                                    _layout_code(rope_layout), float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
            "atf_decode_pack_k")
 
 
 def atf_decode_kcache(q, kcache, v, out=None, *, S: int, rope_base: float, alpha: float, causal: int = 1,
-                      pos0: int = 0, ws=None, return_skipped: bool = False):
+                      pos0: int = 0, ws=None, return_skipped: bool = False, rope_layout="neox"):
     """Decode over the windowed key cache: q [B,Hq,1,d] at pos0+S, v [B,Hkv,cap,d]."""
     B, Hq, one, d = q.shape
     if one != 1:
@@ -294,7 +310,8 @@ def atf_decode_kcache(q, kcache, v, out=None, *, S: int, rope_base: float, alpha
         ws = workspace(nbytes, q.device, "decode")
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_decode_kcache(_dev(q, "q"), _dev(kcache, "kcache"), _dev(v, "v"), _dev(out, "out"),
-                                    B, Hq, Hkv, int(S), cap, d, float(rope_base), float(alpha), int(causal),
+                                    B, Hq, Hkv, int(S), cap, d, _layout_code(rope_layout), float(rope_base),
+                                    float(alpha), int(causal),
                                     int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                     ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode_kcache")
@@ -316,7 +333,8 @@ def _dev_i32(t, name):
     return _dev(t, name)
 
 
-def atf_paged_write(k, v, kpool, vpool, page_table, *, k_begin: int, rope_base: float, pos0: int = 0):
+def atf_paged_write(k, v, kpool, vpool, page_table, *, k_begin: int, rope_base: float, pos0: int = 0,
+                    rope_layout="neox"):
     """Write tokens k_begin.. of every sequence (k, v [B,Hkv,n,d]) into their pages.
     page_table: int32 [B, max_pages] on the device; pools: one page = atf_paged_page_bytes."""
     B, Hkv, n, d = k.shape
@@ -324,12 +342,14 @@ def atf_paged_write(k, v, kpool, vpool, page_table, *, k_begin: int, rope_base: 
     num_pages = kpool.numel() * kpool.element_size() // atf_paged_page_bytes(Hkv, d)
     _check(_lib().atf_paged_write(_dev(k, "k"), _dev(v, "v"), _dev(kpool, "kpool"), _dev(vpool, "vpool"),
                                   _dev_i32(page_table, "page_table"), max_pages, num_pages, B, Hkv, n, int(k_begin),
-                                  d, float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
+                                  d, _layout_code(rope_layout), float(rope_base), int(pos0), _dtype_code(k),
+                                  _stream(k.device)),
            "atf_paged_write")
 
 
 def atf_decode_paged(q, kpool, vpool, page_table, seq_lens, out=None, *, max_len: int, rope_base: float,
-                     alpha: float, causal: int = 1, pos0: int = 0, ws=None, return_skipped: bool = False):
+                     alpha: float, causal: int = 1, pos0: int = 0, ws=None, return_skipped: bool = False,
+                     rope_layout="neox"):
     """Ragged decode over the paged cache: q [B,Hq,1,d]; seq_lens int32 [B] on the device."""
     B, Hq, one, d = q.shape
     if one != 1:
@@ -348,7 +368,8 @@ def atf_decode_paged(q, kpool, vpool, page_table, seq_lens, out=None, *, max_len
     skipped = ctypes.c_uint64(0)
     _check(_lib().atf_decode_paged(_dev(q, "q"), _dev(kpool, "kpool"), _dev(vpool, "vpool"), _dev(out, "out"),
                                    _dev_i32(page_table, "page_table"), _dev_i32(seq_lens, "seq_lens"), max_pages,
-                                   num_pages, B, Hq, Hkv, int(max_len), d, float(rope_base), float(alpha),
+                                   num_pages, B, Hq, Hkv, int(max_len), d, _layout_code(rope_layout),
+                                   float(rope_base), float(alpha),
                                    int(causal), int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                    ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode_paged")

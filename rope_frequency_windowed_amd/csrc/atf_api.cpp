@@ -78,6 +78,8 @@ atf_status check_shape(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
     return ATF_OK;
 }
 
+bool bad_layout(int32_t layout) { return layout != ATF_ROPE_NEOX && layout != ATF_ROPE_GPTJ; }
+
 size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype dtype) {
     if (dtype == ATF_F32) return kHeaderBytes;
     const size_t per = (size_t)B * Hkv * (size_t)padded_keys(S) * d * 2;  // bf16
@@ -189,7 +191,7 @@ atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) 
 // sit at key indices Sk - Sq .. Sk - 1 (positions pos0 + Sk - Sq + i), Sk keys
 // at positions pos0 + j.  Shapes are checked by the caller.
 atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
-                       int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, double rope_base, double alpha,
+                       int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, int32_t layout, double rope_base, double alpha,
                        int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
                        uint64_t *skipped_out, hipStream_t s) {
     if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
@@ -211,6 +213,7 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
     a.q_pos0 = pos0 + (Sk - Sq);
     a.k_pos0 = pos0;
     a.causal = causal;
+    a.gptj = layout;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
@@ -288,10 +291,11 @@ size_t atf_prefill_workspace_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d,
 }
 
 atf_status atf_prefill_prepare_kv(const void *k, const void *v, int32_t B, int32_t Hkv, int64_t S,
-                                  int32_t d, double rope_base, int64_t pos0, atf_dtype dtype,
+                                  int32_t d, int32_t rope_layout, double rope_base, int64_t pos0, atf_dtype dtype,
                                   void *workspace, size_t workspace_bytes, atf_stream_t stream) {
     atf_status st = check_shape(B, Hkv, Hkv, S, d, rope_base, 1.0, 1, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(v)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
         return ATF_ERR_WORKSPACE;
@@ -305,6 +309,7 @@ atf_status atf_prefill_prepare_kv(const void *k, const void *v, int32_t B, int32
     a.S = (int)S;
     a.S_pad = (int)padded_keys(S);
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     theta_table(d, rope_base, a.theta);
     hipStream_t s = (hipStream_t)stream;
     if (dtype == ATF_F32) return hip_status(launch_prep_f32(a, d, s));
@@ -316,46 +321,50 @@ atf_status atf_prefill_prepare_kv(const void *k, const void *v, int32_t B, int32
 }
 
 atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
-                              int32_t Hkv, int64_t S, int32_t d, double rope_base, double alpha,
+                              int32_t Hkv, int64_t S, int32_t d, int32_t rope_layout, double rope_base, double alpha,
                               int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
                               size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
-    return attend_impl(q, k, v, out, B, Hq, Hkv, S, S, d, rope_base, alpha, causal, pos0, dtype, workspace,
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
+    return attend_impl(q, k, v, out, B, Hq, Hkv, S, S, d, rope_layout, rope_base, alpha, causal, pos0, dtype, workspace,
                        workspace_bytes, skipped_out, stream);
 }
 
 atf_status atf_prefill(const void *q, const void *k, const void *v, void *out, int32_t B,
-                       int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double rope_base,
+                       int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t rope_layout, double rope_base,
                        double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
                        void *workspace, size_t workspace_bytes, uint64_t *skipped_out,
                        atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, S, d, dtype))
         return ATF_ERR_WORKSPACE;
-    st = atf_prefill_prepare_kv(k, v, B, Hkv, S, d, rope_base, pos0, dtype, workspace,
+    st = atf_prefill_prepare_kv(k, v, B, Hkv, S, d, rope_layout, rope_base, pos0, dtype, workspace,
                                 workspace_bytes, stream);
     if (st != ATF_OK) return st;
-    return atf_prefill_attend(q, k, v, out, B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype,
+    return atf_prefill_attend(q, k, v, out, B, Hq, Hkv, S, d, rope_layout, rope_base, alpha, causal, pos0, dtype,
                               workspace, workspace_bytes, skipped_out, stream);
 }
 
 atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *out, int32_t B,
-                             int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, double rope_base,
-                             double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
-                             size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+                             int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, int32_t rope_layout,
+                             double rope_base, double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
+                             void *workspace, size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     if (Sq < 1 || Sq > Sk) return ATF_ERR_INVALID_ARG;
     atf_status st = check_shape(B, Hq, Hkv, Sk, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
         return ATF_ERR_WORKSPACE;
-    st = atf_prefill_prepare_kv(k, v, B, Hkv, Sk, d, rope_base, pos0, dtype, workspace, workspace_bytes,
-                                stream);
+    st = atf_prefill_prepare_kv(k, v, B, Hkv, Sk, d, rope_layout, rope_base, pos0, dtype, workspace,
+                                workspace_bytes, stream);
     if (st != ATF_OK) return st;
-    return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_base, alpha, causal, pos0, dtype, workspace,
+    return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_layout, rope_base, alpha, causal, pos0, dtype,
+                       workspace,
                        workspace_bytes, skipped_out, (hipStream_t)stream);
 }
 
@@ -365,11 +374,12 @@ size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S,
 }
 
 atf_status atf_decode(const void *q, const void *k, const void *v, void *out, int32_t B,
-                      int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double rope_base, double alpha,
-                      int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
+                      int32_t Hq, int32_t Hkv, int64_t S, int32_t d, int32_t rope_layout, double rope_base,
+                      double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
                       size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(workspace) || workspace_bytes < decode_ws_bytes(B, Hq, Hkv, S, d))
         return ATF_ERR_WORKSPACE;
@@ -393,6 +403,7 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
         a.q_pos0 = pos0 + S;
         a.k_pos0 = pos0;
         a.causal = 1;  // the query follows every key: both settings see all of them
+        a.gptj = rope_layout;
         a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
         window_table_i32(d, rope_base, alpha, a.W);
         theta_table(d, rope_base, a.theta);
@@ -414,6 +425,7 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
     a.group = Hq / Hkv;
     a.S = (int)S;
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
@@ -433,8 +445,9 @@ size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d) {
 }
 
 atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
-                             int64_t cap, int32_t d, double rope_base, int64_t pos0, atf_dtype dtype,
-                             atf_stream_t stream) {
+                             int64_t cap, int32_t d, int32_t rope_layout, double rope_base, int64_t pos0,
+                             atf_dtype dtype, atf_stream_t stream) {
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!k || !kcache || !aligned16(k) || !aligned16(kcache)) return ATF_ERR_INVALID_ARG;
     if (B < 1 || Hkv < 1 || n < 1 || k_begin < 0) return ATF_ERR_INVALID_ARG;
     if (cap < kKeyTile || cap % kKeyTile != 0 || k_begin + n > cap) return ATF_ERR_INVALID_ARG;
@@ -454,16 +467,18 @@ atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv
     a.cap = (int)cap;
     a.k_begin = k_begin;
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     theta_table(d, rope_base, a.theta);
     return hip_status(launch_kpack_bf16(a, d, (hipStream_t)stream));
 }
 
 atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, void *out, int32_t B,
-                             int32_t Hq, int32_t Hkv, int64_t S, int64_t cap, int32_t d, double rope_base,
-                             double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
-                             size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+                             int32_t Hq, int32_t Hkv, int64_t S, int64_t cap, int32_t d, int32_t rope_layout,
+                             double rope_base, double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
+                             void *workspace, size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, S, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (cap < kKeyTile || cap % kKeyTile != 0 || S > cap || pos0 + cap + 1 >= (int64_t)INT32_MAX)
         return ATF_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(kcache) || !aligned16(v) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
@@ -485,6 +500,7 @@ atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, v
     a.S = (int)S;
     a.cap = (int)cap;
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
@@ -509,8 +525,10 @@ size_t atf_paged_page_bytes(int32_t Hkv, int32_t d) {
 
 atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpool, const int32_t *page_table,
                            int32_t max_pages, int32_t num_pages, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
-                           int32_t d, double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream) {
+                           int32_t d, int32_t rope_layout, double rope_base, int64_t pos0, atf_dtype dtype,
+                           atf_stream_t stream) {
     if (!k || !v || !kpool || !vpool || !page_table) return ATF_ERR_INVALID_ARG;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(v) || !aligned16(kpool) || !aligned16(vpool) ||
         ((uintptr_t)page_table & 3u) != 0)
         return ATF_ERR_INVALID_ARG;
@@ -537,17 +555,19 @@ atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpoo
     a.num_pages = num_pages;
     a.k_begin = k_begin;
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     theta_table(d, rope_base, a.theta);
     return hip_status(launch_paged_write_bf16(a, d, (hipStream_t)stream));
 }
 
 atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool, void *out,
                             const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages, int32_t num_pages,
-                            int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, double rope_base,
-                            double alpha, int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace,
-                            size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
+                            int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, int32_t rope_layout,
+                            double rope_base, double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
+                            void *workspace, size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
     atf_status st = check_shape(B, Hq, Hkv, max_len, d, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!page_table || !seq_lens || ((uintptr_t)page_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
         return ATF_ERR_INVALID_ARG;
     if (max_pages < 1 || num_pages < 1 || max_len > (int64_t)max_pages * kKeyTile) return ATF_ERR_INVALID_ARG;
@@ -574,6 +594,7 @@ atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool,
     a.max_pages = max_pages;
     a.num_pages = num_pages;
     a.pos0 = pos0;
+    a.gptj = rope_layout;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);

@@ -36,6 +36,7 @@ struct PrepArgs {
     unsigned long long *counter;      // zeroed here
     int B, Hkv, S, S_pad;
     long long pos0;
+    int gptj;                         // rotary pairs: 0 = dims (p, p + d/2), 1 = dims (2p, 2p + 1)
     double theta[kMaxPairs];
 };
 
@@ -50,6 +51,7 @@ struct AttnArgs {
     int Sq, Sk, Sk_pad;               // query rows, keys, padded keys
     long long q_pos0, k_pos0;         // position of query 0 and key 0
     int causal;                       // 1: keys at or before the query; 0: all keys, windows on |i - j|
+    int gptj;                         // rotary pairs: 0 = dims (p, p + d/2), 1 = dims (2p, 2p + 1)
     int n_qtiles, n_groups;           // work decomposition
     float scale_log2;                 // log2(e) / sqrt(d)
     int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)
@@ -73,6 +75,7 @@ struct DecodeArgs {
     const int *seq_lens;
     int max_pages, num_pages;
     int split_budget;                 // paged: splits per (kv head, slab) shared by the batch, by length
+    int gptj;                         // rotary pairs of q and k: 0 = (p, p + d/2), 1 = (2p, 2p + 1)
     long long pos0;
     float scale_log2;
     int W[kMaxPairs];
@@ -87,6 +90,7 @@ struct KPackArgs {
     void *kc;                         // the key cache, capacity cap keys per (b, kv head)
     int B, Hkv, n, cap;
     long long k_begin, pos0;          // key k[.., i, :] is cache key k_begin + i at pos0 + k_begin + i
+    int gptj;                         // rotary pairs of k: 0 = (p, p + d/2), 1 = (2p, 2p + 1)
     double theta[kMaxPairs];
 };
 
@@ -102,6 +106,7 @@ struct PagedWriteArgs {
     const int *page_table;            // [B][max_pages]
     int B, Hkv, n, max_pages, num_pages;
     long long k_begin, pos0;          // token i of the call is token k_begin + i, at pos0 + k_begin + i
+    int gptj;                         // rotary pairs of k: 0 = (p, p + d/2), 1 = (2p, 2p + 1)
     double theta[kMaxPairs];
 };
 hipError_t launch_paged_write_bf16(const PagedWriteArgs &a, int d, hipStream_t s);

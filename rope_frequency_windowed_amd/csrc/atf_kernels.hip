@@ -61,6 +61,33 @@ __device__ inline float dot2_bf(unsigned a, unsigned b, float c) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotary pairs off .. off+3 of a bf16 row as two 8-byte pieces.  NeoX
+// half-split layout (pair p = dims p and p + P): lo holds the pairs' first
+// elements, hi their second.  GPT-J interleaved layout (pair p = dims 2p and
+// 2p + 1): lo holds pairs off, off+1 and hi pairs off+2, off+3, each pair one
+// 32-bit word (first element in the low half).
+__device__ inline void load_pair_pieces(const unsigned short *row, int off, int P, bool gptj, u32x2 &lo, u32x2 &hi) {
+    if (gptj) {
+        lo = *(const u32x2 *)(row + 2 * off);
+        hi = *(const u32x2 *)(row + 2 * off + 4);
+    } else {
+        lo = *(const u32x2 *)(row + off);
+        hi = *(const u32x2 *)(row + P + off);
+    }
+}
+// First (x) and second (y) element of pair off + w (w = 0..3) from the pieces.
+__device__ inline void pair_xy(u32x2 lo, u32x2 hi, int w, bool gptj, float &x, float &y) {
+    if (gptj) {
+        const unsigned wd = (w == 0) ? lo.x : (w == 1) ? lo.y : (w == 2) ? hi.x : hi.y;
+        x = __uint_as_float(wd << 16);
+        y = __uint_as_float(wd & 0xffff0000u);
+    } else {
+        const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
+        x = (w & 1) ? __uint_as_float(lw & 0xffff0000u) : __uint_as_float(lw << 16);
+        y = (w & 1) ? __uint_as_float(hw & 0xffff0000u) : __uint_as_float(hw << 16);
+    }
+}
+
 __device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -116,20 +143,16 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
         const int j = tile * kKeyTile + row;
         union { u32x4 v[PPT / 4]; unsigned w[PPT]; } res;
         if (j < a.S) {
-            union { u32x4 v[PPT / 8]; unsigned short s[PPT]; } lo, hi;
             const unsigned short *src = k + (long long)j * D;
-#pragma unroll
-            for (int u = 0; u < PPT / 8; ++u) {
-                lo.v[u] = ((const u32x4 *)(src + p0))[u];
-                hi.v[u] = ((const u32x4 *)(src + P + p0))[u];
-            }
             const long long pos = a.pos0 + j;
+            u32x2 lo[PPT / 4], hi[PPT / 4];
+#pragma unroll
+            for (int g = 0; g < PPT / 4; ++g) load_pair_pieces(src, p0 + 4 * g, P, a.gptj != 0, lo[g], hi[g]);
 #pragma unroll
             for (int u = 0; u < PPT; ++u) {
-                float c, s;
+                float c, s, x, y;
                 rope_cos_sin(pos, a.theta[p0 + u], c, s);
-                const float x = __uint_as_float((unsigned)lo.s[u] << 16);
-                const float y = __uint_as_float((unsigned)hi.s[u] << 16);
+                pair_xy(lo[u / 4], hi[u / 4], u % 4, a.gptj != 0, x, y);
                 res.w[u] = pack_bf(x * c - y * s, y * c + x * s);
             }
         } else {
@@ -453,15 +476,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
             if (q_valid) {
                 const int p0 = 8 * s + 4 * half;
-                const u32x2 lo = *(const u32x2 *)(qrow + p0);
-                const u32x2 hi = *(const u32x2 *)(qrow + P + p0);
+                u32x2 lo, hi;
+                load_pair_pieces(qrow, p0, P, a.gptj != 0, lo, hi);
                 unsigned r[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
-                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
-                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
-                    float c, sn;
+                    float x, y, c, sn;
+                    pair_xy(lo, hi, u, a.gptj != 0, x, y);
                     rope_cos_sin(pos, a.theta[p0 + u], c, sn);
                     r[u] = pack_bf((x * c - y * sn) * sc, (y * c + x * sn) * sc);
                 }
@@ -788,7 +809,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
         for (int p = 0; p < P; ++p) {
             float c, s;
             rope_cos_sin(qpos, a.theta[p], c, s);
-            const float x = valid ? qrow[p] : 0.f, y = valid ? qrow[p + P] : 0.f;
+            const int il = a.gptj ? 2 * p : p, ih = a.gptj ? 2 * p + 1 : p + P;  // the pair's two dims
+            const float x = valid ? qrow[il] : 0.f, y = valid ? qrow[ih] : 0.f;
             qx[p] = x * c - y * s;
             qy[p] = y * c + x * s;
         }
@@ -814,7 +836,8 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
             if (j < kend) {
                 float c, s;
                 rope_cos_sin(a.k_pos0 + j, a.theta[p], c, s);
-                const float x = kh[(long long)j * D + p], y = kh[(long long)j * D + p + P];
+                const int il = a.gptj ? 2 * p : p, ih = a.gptj ? 2 * p + 1 : p + P;
+                const float x = kh[(long long)j * D + il], y = kh[(long long)j * D + ih];
                 r = make_float2(x * c - y * s, y * c + x * s);
             }
             ks[jj][p] = r;
@@ -905,9 +928,10 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char *lds, unsigned byte_ad
     return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D>
+template <int D, bool GPTJ>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
+    constexpr bool QGPTJ = GPTJ;  // rotary layout of q and k
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
     constexpr int CK = 32;               // keys per wave chunk
@@ -955,15 +979,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
             if (t < nh) {
                 const int pb = 16 * s + 4 * q;
-                const u32x2 lo = *(const u32x2 *)(qrow + pb);
-                const u32x2 hi = *(const u32x2 *)(qrow + P + pb);
+                u32x2 lo, hi;
+                load_pair_pieces(qrow, pb, P, QGPTJ, lo, hi);
                 unsigned r[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
-                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
-                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
-                    float c, sn;
+                    float x, y, c, sn;
+                    pair_xy(lo, hi, u, QGPTJ, x, y);
                     rope_cos_sin(qpos, a.theta[pb + u], c, sn);
                     r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
                 }
@@ -1039,9 +1061,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     // Key pieces of the last two K-steps (the only ones far keys keep) are
     // loaded one chunk ahead into registers; nearer steps load on use.  Every
     // load is issued unconditionally (fixed vmcnt bookkeeping, no divergent
-    // branches): a piece the lane does not need reads the key row's last
-    // 8 bytes of each half (pairs P-4..P-1, never cut, so another lane fetches
-    // the same sectors anyway), and the per-pair mask zeroes it.
+    // branches): a piece the lane does not need reads the pieces of pairs
+    // P-4..P-1 (never cut, so another lane fetches the same sectors anyway),
+    // and the per-pair mask zeroes it.  In the interleaved layout a key's kept
+    // pairs are one contiguous suffix of its row.
     constexpr int SPRE = (NSTEP >= 2) ? NSTEP - 2 : 0;
 #define DEC_LOAD_K(jc_, ps0_, ps1_)                                                     \
     {                                                                                 \
@@ -1051,8 +1074,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i) {                \
                 const int pb_ = 16 * (SPRE + i) + 4 * q;                              \
                 const int off_ = (pb_ + 4 > psg_) ? pb_ : (P - 4);                    \
-                klo[g][i] = *(const u32x2 *)(kr_ + off_);                             \
-                khi[g][i] = *(const u32x2 *)(kr_ + P + off_);                         \
+                load_pair_pieces(kr_, off_, P, GPTJ, klo[g][i], khi[g][i]);            \
             }                                                                         \
         }                                                                             \
     }
@@ -1110,16 +1132,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
                     hi = khi[g][s - SPRE];
                 } else {
                     const int off = (pb + 4 > ps) ? pb : (P - 4);
-                    lo = *(const u32x2 *)(krow + off);
-                    hi = *(const u32x2 *)(krow + P + off);
+                    load_pair_pieces(krow, off, P, GPTJ, lo, hi);
                 }
                 unsigned r[4];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const int p = pb + w;
-                    const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
-                    const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
-                    const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
+                    float x, y;
+                    pair_xy(lo, hi, w, GPTJ, x, y);
                     const float2 f = fine[p][u];
                     const float2 cc = coarse[wave][p];
                     const float cs = f.x * cc.x - f.y * cc.y;
@@ -1268,16 +1288,14 @@ __global__ __launch_bounds__(256) void kpack_bf16_kernel(KPackArgs a) {
     for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
         const int i = (int)(e / NPL), pg = (int)(e % NPL);
         const long long j = a.k_begin + i;
-        const unsigned short *src = (const unsigned short *)a.k + ((long long)bk * a.n + i) * D + 4 * pg;
-        const u32x2 lo = *(const u32x2 *)src;
-        const u32x2 hi = *(const u32x2 *)(src + P);
+        const unsigned short *src = (const unsigned short *)a.k + ((long long)bk * a.n + i) * D;
+        u32x2 lo, hi;
+        load_pair_pieces(src, 4 * pg, P, a.gptj != 0, lo, hi);
         unsigned r[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
-            const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
-            const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
-            float c, sn;
+            float x, y, c, sn;
+            pair_xy(lo, hi, w, a.gptj != 0, x, y);
             rope_cos_sin(a.pos0 + j, a.theta[4 * pg + w], c, sn);
             r[w] = pack_bf(x * c - y * sn, y * c + x * sn);
         }
@@ -1308,16 +1326,14 @@ __global__ __launch_bounds__(256) void paged_write_bf16_kernel(PagedWriteArgs a)
         const long long blk = (long long)page * a.Hkv + hk;
         const long long src_row = ((long long)bk * a.n + i) * D;
         if (u < NPL) {
-            const unsigned short *src = (const unsigned short *)a.k + src_row + 4 * u;
-            const u32x2 lo = *(const u32x2 *)src;
-            const u32x2 hi = *(const u32x2 *)(src + P);
+            const unsigned short *src = (const unsigned short *)a.k + src_row;
+            u32x2 lo, hi;
+            load_pair_pieces(src, 4 * u, P, a.gptj != 0, lo, hi);
             unsigned r[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const unsigned lw = (w < 2) ? lo.x : lo.y, hw = (w < 2) ? hi.x : hi.y;
-                const float x = (w & 1) ? bf_hi(lw) : bf_lo(lw);
-                const float y = (w & 1) ? bf_hi(hw) : bf_lo(hw);
-                float c, sn;
+                float x, y, c, sn;
+                pair_xy(lo, hi, w, a.gptj != 0, x, y);
                 rope_cos_sin(a.pos0 + j, a.theta[4 * u + w], c, sn);
                 r[w] = pack_bf(x * c - y * sn, y * c + x * sn);
             }
@@ -1350,6 +1366,7 @@ __global__ __launch_bounds__(256) void paged_write_bf16_kernel(PagedWriteArgs a)
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
+    const bool QGPTJ = a.gptj != 0;  // rotary layout of q (keys are stored rotated)
     constexpr int P = D / 2;
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
@@ -1404,15 +1421,13 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
             if (t < nh) {
                 const int pb = 16 * s + 4 * q;
-                const u32x2 lo = *(const u32x2 *)(qrow + pb);
-                const u32x2 hi = *(const u32x2 *)(qrow + P + pb);
+                u32x2 lo, hi;
+                load_pair_pieces(qrow, pb, P, QGPTJ, lo, hi);
                 unsigned r[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const unsigned lw = (u < 2) ? lo.x : lo.y, hw = (u < 2) ? hi.x : hi.y;
-                    const float x = (u & 1) ? bf_hi(lw) : bf_lo(lw);
-                    const float y = (u & 1) ? bf_hi(hw) : bf_lo(hw);
-                    float c, sn;
+                    float x, y, c, sn;
+                    pair_xy(lo, hi, u, QGPTJ, x, y);
                     rope_cos_sin(qpos, a.theta[pb + u], c, sn);
                     r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
                 }
@@ -1733,8 +1748,10 @@ hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s) {
 hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
-    if (d == 128) decode_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
-    else decode_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
+    if (d == 128 && a.gptj) decode_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) decode_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
+    else if (a.gptj) decode_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
+    else decode_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);

@@ -75,23 +75,23 @@ def test_known_counts(lib):
 
 
 def _call_prefill(lib, **kw):
-    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, base=1e6, alpha=1.0,
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, layout=0, base=1e6, alpha=1.0,
                 causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
     args.update(kw)
     return lib.atf_prefill(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
                            ctypes.c_void_p(args["out"]), args["B"], args["Hq"], args["Hkv"], args["S"],
-                           args["d"], args["base"], args["alpha"], args["causal"], args["pos0"],
+                           args["d"], args["layout"], args["base"], args["alpha"], args["causal"], args["pos0"],
                            args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"],
                            args["stream"])
 
 
 def _call_decode(lib, **kw):
-    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, base=1e6, alpha=1.0,
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, d=128, layout=0, base=1e6, alpha=1.0,
                 causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
     args.update(kw)
     return lib.atf_decode(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]),
                           ctypes.c_void_p(args["out"]), args["B"], args["Hq"], args["Hkv"], args["S"],
-                          args["d"], args["base"], args["alpha"], args["causal"], args["pos0"],
+                          args["d"], args["layout"], args["base"], args["alpha"], args["causal"], args["pos0"],
                           args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"],
                           args["stream"])
 
@@ -121,6 +121,9 @@ BAD = [
     (dict(ws=None), bnd.ATF_ERR_WORKSPACE),
     (dict(ws_bytes=1), bnd.ATF_ERR_WORKSPACE),         # undersized (valid otherwise)
     (dict(Hq=128, Hkv=1), bnd.ATF_ERR_UNSUPPORTED),    # group > 64
+    (dict(layout=2), bnd.ATF_ERR_INVALID_ARG),         # rotary layout: 0 (NeoX) or 1 (GPT-J)
+    (dict(layout=-1), bnd.ATF_ERR_INVALID_ARG),
+    (dict(layout=1), bnd.ATF_ERR_WORKSPACE),           # valid (GPT-J): stops at the workspace
 ]
 
 
@@ -158,12 +161,12 @@ def test_python_binding_needs_gpu_tensors(lib):
 
 
 def _call_chunk(lib, **kw):
-    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, Sq=64, Sk=128, d=128, base=1e6, alpha=1.0,
+    args = dict(q=16, k=32, v=48, out=64, B=1, Hq=4, Hkv=2, Sq=64, Sk=128, d=128, layout=0, base=1e6, alpha=1.0,
                 causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
     args.update(kw)
     return lib.atf_prefill_chunk(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]),
                                  ctypes.c_void_p(args["v"]), ctypes.c_void_p(args["out"]), args["B"],
-                                 args["Hq"], args["Hkv"], args["Sq"], args["Sk"], args["d"], args["base"],
+                                 args["Hq"], args["Hkv"], args["Sq"], args["Sk"], args["d"], args["layout"], args["base"],
                                  args["alpha"], args["causal"], args["pos0"], args["dtype"],
                                  ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"], args["stream"])
 
@@ -187,11 +190,12 @@ def test_kcache_bytes(lib):
 
 
 def _call_pack(lib, **kw):
-    args = dict(k=32, kc=4096, B=1, Hkv=2, n=10, k_begin=0, cap=128, d=128, base=1e6, pos0=0,
+    args = dict(k=32, kc=4096, B=1, Hkv=2, n=10, k_begin=0, cap=128, d=128, layout=0, base=1e6, pos0=0,
                 dtype=atf.ATF_BF16, stream=None)
     args.update(kw)
     return lib.atf_decode_pack_k(ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["kc"]), args["B"], args["Hkv"],
-                                 args["n"], args["k_begin"], args["cap"], args["d"], args["base"], args["pos0"],
+                                 args["n"], args["k_begin"], args["cap"], args["d"], args["layout"], args["base"],
+                                 args["pos0"],
                                  args["dtype"], args["stream"])
 
 
@@ -203,18 +207,19 @@ def _call_pack(lib, **kw):
     (dict(d=96), bnd.ATF_ERR_UNSUPPORTED), (dict(base=1.0), bnd.ATF_ERR_INVALID_ARG),
     (dict(pos0=-1), bnd.ATF_ERR_INVALID_ARG), (dict(pos0=(1 << 31) - 100), bnd.ATF_ERR_INVALID_ARG),
     (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=5), bnd.ATF_ERR_INVALID_ARG),
+    (dict(layout=3), bnd.ATF_ERR_INVALID_ARG),
 ])
 def test_pack_rejects(lib, kw, expect):
     assert _call_pack(lib, **kw) == expect
 
 
 def _call_kcache(lib, **kw):
-    args = dict(q=16, kc=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, cap=128, d=128, base=1e6, alpha=1.0,
+    args = dict(q=16, kc=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, cap=128, d=128, layout=0, base=1e6, alpha=1.0,
                 causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)
     args.update(kw)
     return lib.atf_decode_kcache(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["kc"]),
                                  ctypes.c_void_p(args["v"]), ctypes.c_void_p(args["out"]), args["B"],
-                                 args["Hq"], args["Hkv"], args["S"], args["cap"], args["d"], args["base"],
+                                 args["Hq"], args["Hkv"], args["S"], args["cap"], args["d"], args["layout"], args["base"],
                                  args["alpha"], args["causal"], args["pos0"], args["dtype"],
                                  ctypes.c_void_p(args["ws"]), args["ws_bytes"], args["skipped"], args["stream"])
 
@@ -242,11 +247,12 @@ def test_paged_page_bytes(lib):
 
 def _call_pwrite(lib, **kw):
     args = dict(k=16, v=32, kp=48, vp=64, pt=128, max_pages=4, num_pages=8, B=2, Hkv=2, n=10, k_begin=0, d=128,
-                base=1e6, pos0=0, dtype=atf.ATF_BF16, stream=None)
+                layout=0, base=1e6, pos0=0, dtype=atf.ATF_BF16, stream=None)
     args.update(kw)
     return lib.atf_paged_write(*(ctypes.c_void_p(args[x]) for x in ("k", "v", "kp", "vp", "pt")),
                                args["max_pages"], args["num_pages"], args["B"], args["Hkv"], args["n"],
-                               args["k_begin"], args["d"], args["base"], args["pos0"], args["dtype"], args["stream"])
+                               args["k_begin"], args["d"], args["layout"], args["base"], args["pos0"], args["dtype"],
+                               args["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -256,6 +262,7 @@ def _call_pwrite(lib, **kw):
     (dict(max_pages=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
     (dict(d=96), bnd.ATF_ERR_UNSUPPORTED), (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
     (dict(base=0.5), bnd.ATF_ERR_INVALID_ARG), (dict(pos0=-3), bnd.ATF_ERR_INVALID_ARG),
+    (dict(layout=9), bnd.ATF_ERR_INVALID_ARG),
 ])
 def test_paged_write_rejects(lib, kw, expect):
     assert _call_pwrite(lib, **kw) == expect
@@ -263,12 +270,12 @@ def test_paged_write_rejects(lib, kw, expect):
 
 def _call_pdecode(lib, **kw):
     args = dict(q=16, kp=32, vp=48, out=64, pt=128, sl=256, max_pages=4, num_pages=8, B=2, Hq=4, Hkv=2,
-                max_len=200, d=128, base=1e6, alpha=1.0, causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096,
+                max_len=200, d=128, layout=0, base=1e6, alpha=1.0, causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096,
                 ws_bytes=1, skipped=None, stream=None)
     args.update(kw)
     return lib.atf_decode_paged(*(ctypes.c_void_p(args[x]) for x in ("q", "kp", "vp", "out", "pt", "sl")),
                                 args["max_pages"], args["num_pages"], args["B"], args["Hq"], args["Hkv"],
-                                args["max_len"], args["d"], args["base"], args["alpha"], args["causal"],
+                                args["max_len"], args["d"], args["layout"], args["base"], args["alpha"], args["causal"],
                                 args["pos0"], args["dtype"], ctypes.c_void_p(args["ws"]), args["ws_bytes"],
                                 args["skipped"], args["stream"])
 
@@ -278,8 +285,10 @@ def _call_pdecode(lib, **kw):
     (dict(sl=258), bnd.ATF_ERR_INVALID_ARG), (dict(max_len=257), bnd.ATF_ERR_INVALID_ARG),
     (dict(max_len=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
     (dict(Hq=5), bnd.ATF_ERR_INVALID_ARG), (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
-    (dict(causal=0), bnd.ATF_ERR_WORKSPACE),           # valid (non-causal): stops at the workspace (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(causal=0), bnd.ATF_ERR_WORKSPACE),           # valid (non-causal): stops at the workspace
+    (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED),
     (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG), (dict(ws_bytes=1), bnd.ATF_ERR_WORKSPACE),
+    (dict(layout=2), bnd.ATF_ERR_INVALID_ARG), (dict(layout=1), bnd.ATF_ERR_WORKSPACE),
 ])
 def test_paged_decode_rejects(lib, kw, expect):
     assert _call_pdecode(lib, **kw) == expect
