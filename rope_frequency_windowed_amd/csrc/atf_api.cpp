@@ -63,6 +63,9 @@ void window_table_i32(int d, double base, double alpha, int *Wi) {
 
 bool aligned16(const void *p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
 
+// Head dims with compiled kernels.
+bool supported_d(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
 atf_status check_shape(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, double base,
                        double alpha, int32_t causal, int64_t pos0, atf_dtype dtype) {
     if (B < 1 || Hq < 1 || Hkv < 1 || S < 1) return ATF_ERR_INVALID_ARG;
@@ -73,7 +76,7 @@ atf_status check_shape(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,
     if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return ATF_ERR_INVALID_ARG;
     if (pos0 < 0 || pos0 + S + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return ATF_ERR_UNSUPPORTED;
     if (Hq / Hkv > 64) return ATF_ERR_UNSUPPORTED;
     return ATF_OK;
 }
@@ -229,7 +232,7 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
         const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
         a.krot = ws;
         a.vt = ws + per;
-        a.n_qtiles = (int)((Sq + kQueryTile - 1) / kQueryTile);
+        a.n_qtiles = (int)((Sq + prefill_query_tile(d) - 1) / prefill_query_tile(d));
         a.n_groups = a.n_qtiles * B * Hkv;
         e = launch_prefill_bf16(a, d, s);
     }
@@ -285,7 +288,7 @@ atf_status atf_skipped_pair_products(int64_t S, int32_t d, double rope_base, dou
 }
 
 size_t atf_prefill_workspace_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype dtype) {
-    if (B < 1 || Hkv < 1 || S < 1 || (d != 64 && d != 128)) return 0;
+    if (B < 1 || Hkv < 1 || S < 1 || (!supported_d(d))) return 0;
     if (dtype != ATF_F32 && dtype != ATF_BF16) return 0;
     return prefill_ws_bytes(B, Hkv, S, d, dtype);
 }
@@ -369,7 +372,7 @@ atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *
 }
 
 size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
-    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || (d != 64 && d != 128)) return 0;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S < 1 || (!supported_d(d))) return 0;
     return decode_ws_bytes(B, Hq, Hkv, S, d);
 }
 
@@ -440,7 +443,7 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
 
 size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d) {
     if (B < 1 || Hkv < 1 || cap < kKeyTile || cap % kKeyTile != 0 || cap >= (int64_t)INT32_MAX) return 0;
-    if (d != 64 && d != 128) return 0;
+    if (!supported_d(d)) return 0;
     return (size_t)B * Hkv * (size_t)cap * d * 2;
 }
 
@@ -455,7 +458,7 @@ atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv
     if (!std::isfinite(rope_base) || !(rope_base > 1.0)) return ATF_ERR_INVALID_ARG;
     if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
     if (pos0 < 0 || pos0 + cap + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return ATF_ERR_UNSUPPORTED;
     if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
     KPackArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -519,7 +522,7 @@ size_t atf_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int6
 }
 
 size_t atf_paged_page_bytes(int32_t Hkv, int32_t d) {
-    if (Hkv < 1 || (d != 64 && d != 128)) return 0;
+    if (Hkv < 1 || (!supported_d(d))) return 0;
     return (size_t)Hkv * kKeyTile * d * 2;
 }
 
@@ -539,7 +542,7 @@ atf_status atf_paged_write(const void *k, const void *v, void *kpool, void *vpoo
     if (!std::isfinite(rope_base) || !(rope_base > 1.0)) return ATF_ERR_INVALID_ARG;
     if (dtype != ATF_F32 && dtype != ATF_BF16) return ATF_ERR_INVALID_ARG;
     if (pos0 < 0 || pos0 + cap + 1 >= (int64_t)INT32_MAX) return ATF_ERR_INVALID_ARG;
-    if (d != 64 && d != 128) return ATF_ERR_UNSUPPORTED;
+    if (!supported_d(d)) return ATF_ERR_UNSUPPORTED;
     if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
     PagedWriteArgs a;
     std::memset(&a, 0, sizeof(a));

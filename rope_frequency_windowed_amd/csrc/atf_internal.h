@@ -7,7 +7,7 @@
 
 namespace atf {
 
-constexpr int kMaxPairs = 64;     // d <= 128
+constexpr int kMaxPairs = 128;    // d <= 256
 constexpr int kKeyTile = 64;      // keys per prefill tile / decode chunk
 #ifndef ATF_PREFILL_WAVES
 #define ATF_PREFILL_WAVES 8
@@ -17,7 +17,12 @@ constexpr int kKeyTile = 64;      // keys per prefill tile / decode chunk
 #endif
 constexpr int kPrefillWaves = ATF_PREFILL_WAVES;       // waves per prefill workgroup (bf16)
 constexpr int kPrefillKeys = ATF_PREFILL_KEYS;         // keys per prefill LDS tile (bf16)
-constexpr int kQueryTile = 32 * kPrefillWaves;         // queries per prefill workgroup (bf16)
+// d = 256: a wave's query fragments and output accumulators need one wave per
+// SIMD (512 registers), so 4-wave workgroups; 64-key tiles keep the double
+// buffer at 128 KB of LDS.
+constexpr int prefill_waves(int d) { return d == 256 ? 4 : kPrefillWaves; }
+constexpr int prefill_keys(int d) { return d == 256 ? 64 : kPrefillKeys; }
+constexpr int prefill_query_tile(int d) { return 32 * prefill_waves(d); }  // queries per workgroup (bf16)
 constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
 constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
 constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves

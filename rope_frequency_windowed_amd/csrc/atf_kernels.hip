@@ -75,6 +75,35 @@ __device__ inline void load_pair_pieces(const unsigned short *row, int off, int 
         hi = *(const u32x2 *)(row + P + off);
     }
 }
+// The window table spread over a wave: lane l holds W_l and, for d = 256,
+// W_{l+64} (kWindowInf past the table).  W_p grows with p, so the cut prefix at
+// distance x, #{p : W_p < x}, is one ballot count per half.
+template <int P>
+struct WaveWin {
+    int lo, hi;
+};
+template <int P>
+__device__ inline WaveWin<P> load_windows(const int *W) {
+    const int lane = threadIdx.x & 63;
+    WaveWin<P> w;
+    w.lo = (lane < P) ? W[lane] : kWindowInf;
+    w.hi = (P > 64 && lane + 64 < P) ? W[lane + 64] : kWindowInf;
+    return w;
+}
+template <int P>
+__device__ inline int cut_below(const WaveWin<P> &w, int x) {
+    int n = __builtin_popcountll(__ballot(w.lo < x));
+    if constexpr (P > 64) n += __builtin_popcountll(__ballot(w.hi < x));
+    return n;
+}
+// W_p for a wave-uniform p
+template <int P>
+__device__ inline int window_at(const WaveWin<P> &w, int p) {
+    const int a = __builtin_amdgcn_readlane(w.lo, p & 63);
+    if constexpr (P > 64) return (p < 64) ? a : __builtin_amdgcn_readlane(w.hi, p & 63);
+    return a;
+}
+
 // First (x) and second (y) element of pair off + w (w = 0..3) from the pieces.
 __device__ inline void pair_xy(u32x2 lo, u32x2 hi, int w, bool gptj, float &x, float &y) {
     if (gptj) {
@@ -110,7 +139,9 @@ __device__ inline float wave_sum(float v) {
 __device__ inline int swz8(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 __device__ inline int swz16(int row) { return row & 15; }
 template <int CH>
-__device__ inline int kswz(int row) { return (CH == 16) ? swz16(row) : swz8(row); }
+__device__ inline int kswz(int row) { return (CH >= 16) ? swz16(row) : swz8(row); }
+template <int CH>
+constexpr int kswz_rows() { return (CH >= 16) ? 16 : 8; }  // period of kswz in rows
 
 // ============================================================================
 // Preparation pass (bf16): rotate every key once, store it pair-interleaved
@@ -286,21 +317,14 @@ template <int NSTEP>
 __device__ inline f32x16_t qk_main(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
                                    const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b) {
 #define ATF_CHAIN(s0_) qk_chain<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b)
-    switch (s_first) {
-        case 0: return ATF_CHAIN(0);
-        case 1: return ATF_CHAIN(1);
-        case 2: return ATF_CHAIN(2);
-        case 3: return ATF_CHAIN(3);
-        default: break;
-    }
-    if constexpr (NSTEP > 4) {
-        switch (s_first) {
-            case 4: return ATF_CHAIN(4);
-            case 5: return ATF_CHAIN(5);
-            case 6: return ATF_CHAIN(6);
-            default: return ATF_CHAIN((NSTEP > 4 ? 7 : 3));
-        }
-    }
+    // s_first < NSTEP (the slowest pair is never cut); the last step is also
+    // the fall-through
+#define ATF_C(i) \
+    case i:      \
+        if constexpr ((i) < NSTEP - 1) return ATF_CHAIN((i) < NSTEP - 1 ? (i) : 0); else break;
+    switch (s_first) { ATF_C(0) ATF_C(1) ATF_C(2) ATF_C(3) ATF_C(4) ATF_C(5) ATF_C(6) ATF_C(7)
+                       ATF_C(8) ATF_C(9) ATF_C(10) ATF_C(11) ATF_C(12) ATF_C(13) ATF_C(14) default: break; }
+#undef ATF_C
     return ATF_CHAIN(NSTEP - 1);
 #undef ATF_CHAIN
 }
@@ -366,21 +390,14 @@ __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, 
                                          const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b,
                                          const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
 #define ATF_CHAIN(s0_) qk_chain_probs<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b, sp, pw, lsum)
-    switch (s_first) {
-        case 0: return ATF_CHAIN(0);
-        case 1: return ATF_CHAIN(1);
-        case 2: return ATF_CHAIN(2);
-        case 3: return ATF_CHAIN(3);
-        default: break;
-    }
-    if constexpr (NSTEP > 4) {
-        switch (s_first) {
-            case 4: return ATF_CHAIN(4);
-            case 5: return ATF_CHAIN(5);
-            case 6: return ATF_CHAIN(6);
-            default: return ATF_CHAIN((NSTEP > 4 ? 7 : 3));
-        }
-    }
+    // s_first < NSTEP (the slowest pair is never cut); the last step is also
+    // the fall-through
+#define ATF_C(i) \
+    case i:      \
+        if constexpr ((i) < NSTEP - 1) return ATF_CHAIN((i) < NSTEP - 1 ? (i) : 0); else break;
+    switch (s_first) { ATF_C(0) ATF_C(1) ATF_C(2) ATF_C(3) ATF_C(4) ATF_C(5) ATF_C(6) ATF_C(7)
+                       ATF_C(8) ATF_C(9) ATF_C(10) ATF_C(11) ATF_C(12) ATF_C(13) ATF_C(14) default: break; }
+#undef ATF_C
     return ATF_CHAIN(NSTEP - 1);
 #undef ATF_CHAIN
 }
@@ -404,30 +421,25 @@ __device__ inline void qk_pair(int s_first, const unsigned char *lds, unsigned k
                                f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
 #define ATF_PAIR(s0_) \
     qk_pair_chain<NSTEP, s0_>(lds, kb0, kb1, ky, qf, zero_below, ones_a, negm_b, s0, s1, pw, lsum)
-    switch (s_first) {
-        case 0: ATF_PAIR(0); return;
-        case 1: ATF_PAIR(1); return;
-        case 2: ATF_PAIR(2); return;
-        default: break;
-    }
-    if constexpr (NSTEP > 4) {
-        switch (s_first) {
-            case 3: ATF_PAIR(3); return;
-            case 4: ATF_PAIR(4); return;
-            case 5: ATF_PAIR(5); return;
-            case 6: ATF_PAIR(6); return;
-            default: ATF_PAIR((NSTEP > 4 ? 7 : 3)); return;
-        }
-    }
+    // s_first < NSTEP (the slowest pair is never cut); the last step is also
+    // the fall-through
+#define ATF_C(i)                                                        \
+    case i:                                                             \
+        if constexpr ((i) < NSTEP - 1) { ATF_PAIR((i) < NSTEP - 1 ? (i) : 0); return; } else break;
+    switch (s_first) { ATF_C(0) ATF_C(1) ATF_C(2) ATF_C(3) ATF_C(4) ATF_C(5) ATF_C(6) ATF_C(7)
+                       ATF_C(8) ATF_C(9) ATF_C(10) ATF_C(11) ATF_C(12) ATF_C(13) ATF_C(14) default: break; }
+#undef ATF_C
     ATF_PAIR(NSTEP - 1);
 #undef ATF_PAIR
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(prefill_waves(D) * 64, D == 256 ? 1 : 8 / kPrefillWaves) void prefill_bf16_kernel(
+    AttnArgs a) {
     constexpr int P = D / 2;
-    constexpr int NW = kPrefillWaves;  // waves per workgroup (two per SIMD)
-    constexpr int KT = kPrefillKeys;   // keys per LDS tile
+    constexpr int NW = prefill_waves(D);  // waves per workgroup (two per SIMD; one at d = 256)
+    constexpr int KT = prefill_keys(D);   // keys per LDS tile
+    constexpr int QT = 32 * NW;           // queries per workgroup
     constexpr int NB = KT / 32;        // 32-key score blocks per tile
     constexpr int NSTEP = D / 16;      // MFMA K-steps of 16 dims (8 pairs)
     constexpr int CH = D / 8;          // 16-byte chunks per rotated-key row
@@ -453,15 +465,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, half = lane >> 5;
-    const int i0 = qt * kQueryTile + wave * 32;  // first query row of this wave
+    const int i0 = qt * QT + wave * 32;  // first query row of this wave
     const int my_q = i0 + qi;
     const bool q_valid = my_q < a.Sq;
     // Causal tests and distances run in key-index units: query row i sits at
     // key index i + qoff (qoff = Sk - Sq > 0 when a prefix of cached keys
     // precedes the query chunk).
     const int qoff = (int)(a.q_pos0 - a.k_pos0);
-    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * kQueryTile + qoff;
-    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
+    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QT + qoff;
+    const WaveWin<P> win = load_windows<P>(a.W);
 
     // ---- this lane's rotated, pre-scaled query in B-operand order: step s
     // holds pairs 8s + 4*half + (0..3), each as (x'_p, x'_{p+P}) * log2(e)/sqrt(d)
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     // causal: keys up to the workgroup's last query; otherwise every key, the
     // windows applying to |i - j|
-    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + kQueryTile - 1) : a.Sk - 1;
+    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
@@ -504,34 +516,44 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     // so the lane fetches the global chunk that the swizzle puts there.  Key
     // chunks whose pairs no block of this workgroup can use are not fetched
     // (c_min: first 16-byte chunk any wave reads in this tile).
-    // Piece n of wave w is tile piece n*NW + w, so every piece of a lane has
-    // the same swizzle: one per-lane offset, plus n * NW KB in a scalar.
-    unsigned k_goff, v_goff;
-    int k_chunk;
+    // Piece n of wave w is tile piece n*NW + w.  When the piece stride covers
+    // whole swizzle periods every piece of a lane has the same swizzle (one
+    // per-lane offset plus n * NW KB in a scalar); otherwise (d = 256) the lane
+    // has KPER offsets, piece n using offset n % KPER.
+    constexpr int KPERIOD = CH * 16 * kswz_rows<CH>();  // bytes of one key-swizzle period
+    constexpr int KPER = (KPERIOD > NW * 1024) ? KPERIOD / (NW * 1024) : 1;
+    static_assert((NW * 1024) % KPERIOD == 0 || KPERIOD % (NW * 1024) == 0, "piece stride vs key swizzle");
+    static_assert((NW * 1024) % (128 * 8) == 0, "a piece stride must keep the value-row swizzle");
+    unsigned k_goff[KPER], v_goff;
+    int k_chunk[KPER];
+#pragma unroll
+    for (int e = 0; e < KPER; ++e) {
+        const int kbyte = (e * NW + wave) * 1024 + lane * 16;
+        const int krow = kbyte / (CH * 16);
+        k_chunk[e] = ((kbyte / 16) % CH) ^ kswz<CH>(krow);
+        k_goff[e] = (unsigned)(krow * (CH * 16) + k_chunk[e] * 16) - (unsigned)(e * NW * 1024);
+    }
     {
         const int kbyte = wave * 1024 + lane * 16;
-        const int krow = kbyte / (CH * 16);
-        k_chunk = ((kbyte / 16) % CH) ^ kswz<CH>(krow);
-        k_goff = (unsigned)(krow * (CH * 16) + k_chunk * 16);
         const int vrow = kbyte / 128;
         v_goff = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
     }
-    static_assert((NW * 1024) % (CH * 16 * 16) == 0 && (NW * 1024) % (128 * 16) == 0,
-                  "a piece stride must keep the row swizzles");
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 #define ATF_TILE_LOAD(kt_, buf_)                                                           \
     {                                                                                      \
         const int j0_ = (kt_) * KT;                                                        \
         const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
-                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + kQueryTile - 1))); \
-        const int c_min_ = 2 * (__builtin_popcountll(__ballot(w_lane < dmin_wg_)) >> 3);   \
+                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QT - 1))); \
+        const int c_min_ = 2 * (cut_below(win, dmin_wg_) >> 3);                            \
         /* a key chunk below c_min is not fetched: its offset is past the buffer's end */ \
-        const unsigned koff_ = (k_chunk >= c_min_) ? k_goff : KT_BYTES;                    \
+        unsigned koff_[KPER];                                                              \
+        _Pragma("unroll") for (int e = 0; e < KPER; ++e)                                   \
+            koff_[e] = (k_chunk[e] >= c_min_) ? k_goff[e] : KT_BYTES;                      \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
         unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * 1024;                    \
         _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
-            lds_dma16_buf(kr_, koff_, n * NW * 1024, lk_ + n * NW * 1024);                 \
+            lds_dma16_buf(kr_, koff_[n % KPER], n * NW * 1024, lk_ + n * NW * 1024);       \
             lds_dma16_buf(vr_, v_goff, n * NW * 1024, lk_ + KT_BYTES + n * NW * 1024);     \
         }                                                                                  \
     }
@@ -634,8 +656,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                 fast = false;
                 dmin = dmax = 0;
             }
-            const int plo_t = __builtin_popcountll(__ballot(w_lane < dmin));
-            p_t = __builtin_popcountll(__ballot(w_lane < dmax));
+            const int plo_t = cut_below(win, dmin);
+            p_t = cut_below(win, dmax);
             fast = fast && plo_t == p_t;
         }
         if (CAUSAL && fast) {
@@ -667,8 +689,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             live[kb] = CAUSAL ? dhi >= 0 : jb < a.Sk;
             const int amin = CAUSAL ? max(0, dlo) : max(0, max(dlo, -dhi));
             const int amax = CAUSAL ? dhi : max(dhi, -dlo);
-            p_lo[kb] = __builtin_popcountll(__ballot(w_lane < amin));
-            p_full[kb] = __builtin_popcountll(__ballot(w_lane < amax));
+            p_lo[kb] = cut_below(win, amin);
+            p_full[kb] = cut_below(win, amax);
         }
 
         // boundary pairs (one rank-2 MFMA each, added where the distance is
@@ -705,7 +727,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                             const f32x16_t tp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(          \
                                 __builtin_bit_cast(bf16x8_t, kw), qf[s], zero16, 0, 0, 0);        \
                             /* pair p is kept iff |dq - c_r| <= W_p: lim <= c_r <= him */      \
-                            const int wp = __builtin_amdgcn_readlane(w_lane, p);                  \
+                            const int wp = window_at(win, p);                                     \
                             const int lim = dq - wp, him = CAUSAL ? dq : dq + wp;                 \
                             _Pragma("unroll") for (int r = 0; r < 16; ++r) {                      \
                                 const int c = 8 * (r >> 2) + (r & 3);                             \
@@ -967,7 +989,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         rope_cos_sin(4 * CK, a.theta[tid], c, s);
         stride_cs[tid] = make_float2(c, s);
     }
-    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
+    const WaveWin<P> win = load_windows<P>(a.W);
 
     // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
     // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
@@ -1045,12 +1067,12 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     {                                                                                 \
         const int d_near_ = a.S - min((jc_) + CK - 1, ke - 1);                        \
         const int d_far_ = a.S - (jc_);                                               \
-        const int p_near_ = __builtin_popcountll(__ballot(w_lane < d_near_));         \
+        const int p_near_ = cut_below(win, d_near_);                                  \
         smin_ = p_near_ >> 4;                                                         \
         ps0_ = p_near_;                                                               \
         ps1_ = p_near_;                                                               \
         for (int pp = p_near_; pp < P - 1; ++pp) {                                    \
-            const int wpp = __builtin_amdgcn_readlane(w_lane, pp);                    \
+            const int wpp = window_at(win, pp);                                       \
             if (wpp >= d_far_) break;                                                 \
             ps0_ += (wpp < a.S - ((jc_) + t)) ? 1 : 0;                                \
             ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;                           \
@@ -1087,10 +1109,16 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         DEC_CHUNK_KEYS(j0, s_min, ps0, ps1);
         DEC_LOAD_K(j0, ps0, ps1);
     }
-    // coarse angle of this lane's pair at the wave's current chunk start:
-    // exact every 16 chunks, advanced by one wave stride in between
-    float2 cs_lane = make_float2(1.f, 0.f), cs_step = make_float2(1.f, 0.f);
-    if (lane < P) cs_step = stride_cs[lane];
+    // coarse angle of this lane's pairs (lane, lane + 64, ...) at the wave's
+    // current chunk start: exact every 16 chunks, advanced by one wave stride
+    // in between
+    constexpr int PPL = (P + 63) / 64;  // pairs per lane
+    float2 cs_lane[PPL], cs_step[PPL];
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        cs_lane[e] = make_float2(1.f, 0.f);
+        cs_step[e] = (lane + 64 * e < P) ? stride_cs[lane + 64 * e] : make_float2(1.f, 0.f);
+    }
     for (int it = 0; j0 < ke; j0 += 4 * CK, ++it) {
         const int jn = j0 + 4 * CK;
         // this chunk's values to LDS (the previous chunk's transposed reads,
@@ -1099,16 +1127,20 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
         for (int m = 0; m < NVP; ++m) *(u32x4 *)(vb + m * 1024 + lane * 16) = vreg[m];
         if (jn < ke) DEC_LOAD_V(jn);
-        if (lane < P) {
-            if ((it & 15) == 0) {
-                float c, s;
-                rope_cos_sin(a.pos0 + j0, a.theta[lane], c, s);
-                cs_lane = make_float2(c, s);
-            } else {
-                cs_lane = make_float2(cs_lane.x * cs_step.x - cs_lane.y * cs_step.y,
-                                      cs_lane.y * cs_step.x + cs_lane.x * cs_step.y);
+#pragma unroll
+        for (int e = 0; e < PPL; ++e) {
+            const int pl = lane + 64 * e;
+            if (pl < P) {
+                if ((it & 15) == 0) {
+                    float c, s;
+                    rope_cos_sin(a.pos0 + j0, a.theta[pl], c, s);
+                    cs_lane[e] = make_float2(c, s);
+                } else {
+                    cs_lane[e] = make_float2(cs_lane[e].x * cs_step[e].x - cs_lane[e].y * cs_step[e].y,
+                                             cs_lane[e].y * cs_step[e].x + cs_lane[e].x * cs_step[e].y);
+                }
+                coarse[wave][pl] = cs_lane[e];
             }
-            coarse[wave][lane] = cs_lane;
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -1261,14 +1293,14 @@ __device__ inline int paged_nsplit(const DecodeArgs &a, int b) { return paged_ns
 
 // Algorithmic bytes of keys [0, j) of a sequence of S keys (decode query after
 // them): 2d per value row plus 4 per kept pair, where pair p (finite W_p) is
-// dropped for the keys j' < S - W_p.  Lane p holds W_p (kWindowInf past the
-// table); every lane returns the sum.
+// dropped for the keys j' < S - W_p.  Every lane returns the sum.
 template <int D>
-__device__ inline long long dec_prefix_bytes(int j, int S, int w_lane) {
+__device__ inline long long dec_prefix_bytes(int j, int S, const WaveWin<D / 2> &win) {
     constexpr int P = D / 2;
     const int lane = threadIdx.x & 63;
     long long dropped = 0;
-    if (lane < P - 1 && w_lane != kWindowInf) dropped = min(j, max(0, S - w_lane));
+    if (lane < P - 1 && win.lo != kWindowInf) dropped = min(j, max(0, S - win.lo));
+    if (P > 64 && lane + 64 < P - 1 && win.hi != kWindowInf) dropped += min(j, max(0, S - win.hi));
     dropped = (long long)wave_sum_u64((unsigned long long)dropped);
     return (long long)j * (2 * D + 4 * P) - 4 * dropped;
 }
@@ -1409,7 +1441,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     const int S = PAGED ? min(max(a.seq_lens[b], 1), a.S) : a.S;
     const long long qpos = a.pos0 + S;
 
-    const int w_lane = (lane < P) ? a.W[lane] : kWindowInf;
+    const WaveWin<P> win = load_windows<P>(a.W);
 
     // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
     // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
@@ -1444,14 +1476,14 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         // planner): split s of nsb starts at the first 64-key chunk whose
         // prefix of algorithmic bytes reaches s / nsb of the total; splits past
         // nsb have no keys
-        const long long total = dec_prefix_bytes<D>(S, S, w_lane);
+        const long long total = dec_prefix_bytes<D>(S, S, win);
         const int nchunks = (S + kKeyTile - 1) / kKeyTile;
         auto start_of = [&](int sp) {
             const long long target = total * min(sp, nsb) / nsb;
             int lo = 0, hi = nchunks;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (dec_prefix_bytes<D>(min(S, mid * kKeyTile), S, w_lane) < target) lo = mid + 1; else hi = mid;
+                if (dec_prefix_bytes<D>(min(S, mid * kKeyTile), S, win) < target) lo = mid + 1; else hi = mid;
             }
             return lo * kKeyTile;
         };
@@ -1519,13 +1551,13 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     {                                                                                 \
         const int d_near_ = S - min((jc_) + CK - 1, ke - 1);                          \
         const int d_far_ = S - (jc_);                                                 \
-        const int p_near_ = __builtin_popcountll(__ballot(w_lane < d_near_));         \
+        const int p_near_ = cut_below(win, d_near_);                                  \
         smin_ = p_near_ >> 4;                                                         \
         pmin = p_near_ >> 2;                                                          \
         ps0_ = p_near_;                                                               \
         ps1_ = p_near_;                                                               \
         for (int pp = p_near_; pp < P - 1; ++pp) {                                    \
-            const int wpp = __builtin_amdgcn_readlane(w_lane, pp);                    \
+            const int wpp = window_at(win, pp);                                       \
             if (wpp >= d_far_) break;                                                 \
             ps0_ += (wpp < S - ((jc_) + t)) ? 1 : 0;                                  \
             ps1_ += (wpp < S - ((jc_) + 16 + t)) ? 1 : 0;                             \
@@ -1690,7 +1722,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // grid B*Hq, block D.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int row = blockIdx.x, c = threadIdx.x;
     const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
     const int ns = PAGED ? paged_nsplit(a, row / a.Hq) : a.nsplit;
@@ -1716,7 +1748,8 @@ __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
 
 hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s) {
     dim3 grid((unsigned)(a.S_pad / kKeyTile), (unsigned)(a.B * a.Hkv));
-    if (d == 128) prep_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    if (d == 256) prep_bf16_kernel<256><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) prep_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else prep_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1729,18 +1762,21 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
     if (a.causal) {
-        if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        if (d == 256) prefill_bf16_kernel<256, true><<<n_wg, prefill_waves(256) * 64, 0, s>>>(a);
+        else if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, prefill_waves(128) * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, true><<<n_wg, prefill_waves(64) * 64, 0, s>>>(a);
     } else {
-        if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        if (d == 256) prefill_bf16_kernel<256, false><<<n_wg, prefill_waves(256) * 64, 0, s>>>(a);
+        else if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, prefill_waves(128) * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, false><<<n_wg, prefill_waves(64) * 64, 0, s>>>(a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s) {
     dim3 grid((unsigned)((a.Sq + 63) / 64), (unsigned)(a.B * a.Hq));
-    if (d == 128) attend_f32_kernel<128><<<grid, 64, 0, s>>>(a);
+    if (d == 256) attend_f32_kernel<256><<<grid, 64, 0, s>>>(a);
+    else if (d == 128) attend_f32_kernel<128><<<grid, 64, 0, s>>>(a);
     else attend_f32_kernel<64><<<grid, 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1748,13 +1784,16 @@ hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s) {
 hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
-    if (d == 128 && a.gptj) decode_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    if (d == 256 && a.gptj) decode_bf16_kernel<256, true><<<grid, 256, 0, s>>>(a);
+    else if (d == 256) decode_bf16_kernel<256, false><<<grid, 256, 0, s>>>(a);
+    else if (d == 128 && a.gptj) decode_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
     else if (d == 128) decode_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
     else if (a.gptj) decode_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
     else decode_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
+    if (d == 256) decode_combine_kernel<256, false><<<a.B * a.Hq, 256, 0, s>>>(a);
+    else if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
     else decode_combine_kernel<64, false><<<a.B * a.Hq, 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1763,7 +1802,8 @@ hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s) {
     const long long total = (long long)a.n * (d / 8);
     const unsigned gx = (unsigned)std::min<long long>((total + 255) / 256, 65535);
     dim3 grid(gx, (unsigned)(a.B * a.Hkv));
-    if (d == 128) kpack_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    if (d == 256) kpack_bf16_kernel<256><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) kpack_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else kpack_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1772,7 +1812,8 @@ hipError_t launch_paged_write_bf16(const PagedWriteArgs &a, int d, hipStream_t s
     const long long total = (long long)a.n * (d / 8 + d / 8);
     const unsigned gx = (unsigned)std::min<long long>((total + 255) / 256, 65535);
     dim3 grid(gx, (unsigned)(a.B * a.Hkv));
-    if (d == 128) paged_write_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
+    if (d == 256) paged_write_bf16_kernel<256><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) paged_write_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else paged_write_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1782,11 +1823,13 @@ hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
     // paged: x walks the batch's splits (at most budget + B of them), y = (kv head, slab)
     grid = dim3((unsigned)(a.split_budget + a.B), (unsigned)(a.Hkv * a.n_slabs));
-    if (d == 128) decode_kcache_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
+    if (d == 256) decode_kcache_bf16_kernel<256, true><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) decode_kcache_bf16_kernel<128, true><<<grid, 256, 0, s>>>(a);
     else decode_kcache_bf16_kernel<64, true><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d == 128) decode_combine_kernel<128, true><<<a.B * a.Hq, 128, 0, s>>>(a);
+    if (d == 256) decode_combine_kernel<256, true><<<a.B * a.Hq, 256, 0, s>>>(a);
+    else if (d == 128) decode_combine_kernel<128, true><<<a.B * a.Hq, 128, 0, s>>>(a);
     else decode_combine_kernel<64, true><<<a.B * a.Hq, 64, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1794,11 +1837,13 @@ hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s) {
 hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
-    if (d == 128) decode_kcache_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
+    if (d == 256) decode_kcache_bf16_kernel<256, false><<<grid, 256, 0, s>>>(a);
+    else if (d == 128) decode_kcache_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);
     else decode_kcache_bf16_kernel<64, false><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
+    if (d == 256) decode_combine_kernel<256, false><<<a.B * a.Hq, 256, 0, s>>>(a);
+    else if (d == 128) decode_combine_kernel<128, false><<<a.B * a.Hq, 128, 0, s>>>(a);
     else decode_combine_kernel<64, false><<<a.B * a.Hq, 64, 0, s>>>(a);
     return hipGetLastError();
 }

@@ -107,7 +107,8 @@ BAD = [
     (dict(S=0), bnd.ATF_ERR_INVALID_ARG),
     (dict(d=63), bnd.ATF_ERR_INVALID_ARG),
     (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
-    (dict(d=256), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(d=256), bnd.ATF_ERR_WORKSPACE),              # valid: stops at the workspace
+    (dict(d=512), bnd.ATF_ERR_UNSUPPORTED),
     (dict(base=1.0), bnd.ATF_ERR_INVALID_ARG),
     (dict(base=float("inf")), bnd.ATF_ERR_INVALID_ARG),
     (dict(alpha=0.0), bnd.ATF_ERR_INVALID_ARG),
@@ -185,7 +186,9 @@ def test_chunk_rejects_bad_lengths(lib, kw):
 def test_kcache_bytes(lib):
     assert atf.atf_decode_kcache_bytes(8, 4, 262144, 128) == 8 * 4 * 262144 * 128 * 2
     assert atf.atf_decode_kcache_bytes(1, 1, 64, 64) == 64 * 64 * 2
-    for bad in [(1, 1, 100, 128), (1, 1, 0, 128), (0, 1, 64, 128), (1, 1, 64, 96), (1, 1, 1 << 31, 128)]:
+    assert atf.atf_decode_kcache_bytes(2, 1, 128, 256) == 2 * 128 * 256 * 2
+    for bad in [(1, 1, 100, 128), (1, 1, 0, 128), (0, 1, 64, 128), (1, 1, 64, 96), (1, 1, 1 << 31, 128),
+                (1, 1, 64, 512)]:
         assert atf.atf_decode_kcache_bytes(*bad) == 0
 
 
@@ -243,6 +246,7 @@ def test_paged_page_bytes(lib):
     assert atf.atf_paged_page_bytes(4, 128) == 4 * 64 * 128 * 2
     assert atf.atf_paged_page_bytes(1, 64) == 64 * 64 * 2
     assert atf.atf_paged_page_bytes(0, 128) == 0 and atf.atf_paged_page_bytes(2, 96) == 0
+    assert atf.atf_paged_page_bytes(2, 256) == 2 * 64 * 256 * 2
 
 
 def _call_pwrite(lib, **kw):

@@ -41,7 +41,7 @@ def test_window_closed_forms(orc):
     assert n >= 20
 
 
-@pytest.mark.parametrize("d,base", [(64, 1e4), (128, 1e6), (128, 1e4), (16, 10.0)])
+@pytest.mark.parametrize("d,base", [(64, 1e4), (128, 1e6), (128, 1e4), (16, 10.0), (256, 1e6), (256, 1e4)])
 @pytest.mark.parametrize("alpha", [0.25, 0.5, 1.0, 2.0, 7.5])
 def test_window_structure(orc, d, base, alpha):
     W = orc.window_table(d, base, alpha)
@@ -93,7 +93,8 @@ def brute_force_count(W, q_pos, k_pos, causal=True):
 
 @pytest.mark.parametrize("S,d,base,alpha", [(64, 16, 10.0, 0.3), (200, 16, 10.0, 1.0),
                                             (256, 64, 1e4, 1.0), (97, 32, 100.0, 0.7),
-                                            (2048, 64, 1e4, 1.0), (1500, 128, 1e6, 0.5)])
+                                            (2048, 64, 1e4, 1.0), (1500, 128, 1e6, 0.5),
+                                            (3000, 256, 1e4, 1.0)])
 def test_count_closed_form_equals_brute_force(orc, S, d, base, alpha):
     W = orc.window_table(d, base, alpha)
     pos = np.arange(S)
@@ -146,6 +147,16 @@ def test_alpha_inf_equals_dense(orc, causal):
     q, k, v = rnd((B, Hq, S, d), 11), rnd((B, Hkv, S, d), 12), rnd((B, Hkv, S, d), 13)
     out, skipped = orc.attention(q, k, v, base=1e4, alpha=math.inf, causal=causal, q_pos0=5, k_pos0=5)
     ref = dense_ref.dense_rope_attention(q, k, v, base=1e4, causal=causal, q_pos0=5, k_pos0=5)
+    assert skipped == 0
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+
+
+def test_alpha_inf_equals_dense_d256(orc):
+    """d = 256 (128 pairs, more than a wave's 64 lanes on the GPU side)."""
+    B, Hq, Hkv, S, d = 1, 2, 1, 60, 256
+    q, k, v = rnd((B, Hq, S, d), 14), rnd((B, Hkv, S, d), 15), rnd((B, Hkv, S, d), 16)
+    out, skipped = orc.attention(q, k, v, base=1e4, alpha=math.inf)
+    ref = dense_ref.dense_rope_attention(q, k, v, base=1e4)
     assert skipped == 0
     np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
 
