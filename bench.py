@@ -15,7 +15,7 @@ algorithmic flops count only the pair products the windows keep plus P.V);
 against their roofline; `cpu_baseline` is the fp64 oracle timed on a bounded
 sample on the host.
 
-  python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache|paged] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache|paged|variants] [--no-cpu]
   python bench.py --copy-probe      (plain copy kernel of known size, for the
                                      HBM-counter scale factor)
 """
@@ -43,6 +43,10 @@ PAGED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_paged_kv262144_coun
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
+# variant legs (the interleaved rotary layout and 256-dim heads), timed on
+# their own after the main step
+PREFILL_D256 = dict(B=1, Hq=28, Hkv=4, S=32768, d=256, base=1e6, alpha=1.0)
+DECODE_D256 = dict(B=8, Hq=28, Hkv=4, S=65536, d=256, base=1e6, alpha=1.0)
 
 
 def log(*a):
@@ -141,12 +145,83 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 5}))
 
 
+def time_leg(torch, stream, fn, steps):
+    """Average ms of fn() over `steps` calls (one untimed call first), HIP events
+    on the library's stream."""
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps
+
+
+def variant_legs(atf, torch, make_qkv, dev, stream, steps):
+    """Decode at the main decode size with GPT-J interleaved pairs (standard
+    [S][d] cache), and prefill/decode with 256-dim heads."""
+    out = {}
+    D = DECODE
+    q, k, v = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(atf.atf_decode_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
+                     dtype=torch.uint8, device=dev)
+    ms = time_leg(torch, stream, lambda: atf.atf_decode(q, k, v, o, rope_base=D["base"], alpha=D["alpha"], ws=ws,
+                                                        rope_layout="gptj"), steps)
+    nbytes = decode_algorithmic_bytes(atf, **D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["decode_gptj"] = {"value": gbs, "unit": "GB/s", "ms": ms, "config": dict(D, rope_layout="gptj"),
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+    log("decode (GPT-J layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+    del q, k, v, o, ws
+
+    P = PREFILL_D256
+    q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], P["S"], P["S"], P["d"], dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], P["S"], P["d"], atf.ATF_BF16),
+                     dtype=torch.uint8, device=dev)
+    atf.atf_prefill_prepare_kv(k, v, rope_base=P["base"], ws=ws)
+    got = atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=P["alpha"], ws=ws, return_skipped=True)
+    if got != P["B"] * P["Hq"] * atf.atf_skipped_pair_products(P["S"], P["d"], P["base"], P["alpha"]):
+        raise SystemExit("d=256 prefill dropped-term count differs from the closed form")
+    ms = time_leg(torch, stream, lambda: atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=P["alpha"],
+                                                                ws=ws), steps)
+    flops = prefill_algorithmic_flops(atf, **P)
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_d256"] = {"value": P["B"] * P["S"] / (ms * 1e-3), "unit": "tok/s (attention kernel)", "ms": ms,
+                           "config": P,
+                           "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                        "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                        "algorithmic_flops_per_launch": flops}}
+    log("prefill d=256 S=%d: attend %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
+        % (P["S"], ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+    del q, k, v, o, ws
+
+    D = DECODE_D256
+    q, k, v = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(atf.atf_decode_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
+                     dtype=torch.uint8, device=dev)
+    ms = time_leg(torch, stream, lambda: atf.atf_decode(q, k, v, o, rope_base=D["base"], alpha=D["alpha"], ws=ws),
+                  steps)
+    nbytes = decode_algorithmic_bytes(atf, **D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["decode_d256"] = {"value": gbs, "unit": "GB/s", "ms": ms, "config": D,
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+    log("decode d=256 KV=%d: %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (D["S"], ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--only", choices=["prefill", "decode", "kcache", "paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "kcache", "paged", "variants"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -170,6 +245,7 @@ def main():
     do_decode = args.only in (None, "decode")
     do_kcache = args.only in (None, "kcache")
     do_paged = args.only in (None, "paged")
+    do_variants = args.only in (None, "variants")
 
     if do_prefill:
         P = PREFILL
@@ -324,6 +400,10 @@ def main():
             % (pg_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
         if args.only == "paged":
             res["value"], res["unit"] = gbs, "GB/s"
+    if do_variants:
+        res["variants"] = variant_legs(atf, torch, make_qkv, dev, stream, args.steps)
+        if args.only == "variants":
+            res["value"], res["unit"] = res["variants"]["decode_gptj"]["value"], "GB/s"
     res["config"] = config
     if do_prefill and not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(q, k, v, PREFILL)

@@ -97,41 +97,44 @@ struct DecodePlan {
     int starts[kMaxSplits + 1];
 };
 
-int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S) {
+// Decode workgroups resident at once: 2 per CU x 256 CUs; at d = 256 the
+// kernels' registers allow one per CU.
+int64_t decode_resident(int32_t d) { return d == 256 ? 256 : 512; }
+
+int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
     const int group = Hq / Hkv;
     const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
     const int64_t units = (int64_t)B * Hkv * n_slabs;
     const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
-    // aim for one round of resident workgroups: the kernel's registers allow
-    // 2 workgroups (8 waves) per CU, x 256 CUs = 512; byte-balanced splits then
+    // aim for one round of resident workgroups; byte-balanced splits then
     // finish together.  At least one chunk per split.
-    int64_t ns = (512 + units - 1) / units;
+    int64_t ns = (decode_resident(d) + units - 1) / units;
     ns = std::min<int64_t>(ns, kMaxSplits);
     ns = std::min<int64_t>(ns, nchunks);
     return (int)std::max<int64_t>(ns, 1);
 }
 
 size_t decode_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
-    const int ns = decode_nsplit(B, Hq, Hkv, S);
+    const int ns = decode_nsplit(B, Hq, Hkv, S, d);
     return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
 // Paged, ragged decode: the batch shares a budget of ~512 workgroups per call
 // (one round of resident workgroups) in proportion to the sequences' lengths;
 // one sequence may take all of it.  The grid is that per-sequence maximum wide.
-void paged_plan(int32_t Hq, int32_t Hkv, int64_t max_len, int &budget, int &nsplit_max) {
+void paged_plan(int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, int &budget, int &nsplit_max) {
     const int group = Hq / Hkv;
     const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
     const int64_t units = (int64_t)Hkv * n_slabs;
     const int64_t nchunks = (max_len + kKeyTile - 1) / kKeyTile;
-    const int64_t b = std::max<int64_t>(1, (512 + units - 1) / units);
+    const int64_t b = std::max<int64_t>(1, (decode_resident(d) + units - 1) / units);
     budget = (int)b;
     nsplit_max = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(b, kMaxSplits), nchunks));
 }
 
 size_t paged_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d) {
     int budget, ns;
-    paged_plan(Hq, Hkv, max_len, budget, ns);
+    paged_plan(Hq, Hkv, max_len, d, budget, ns);
     return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
@@ -157,7 +160,7 @@ void plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d, const
     const int P = d / 2;
     const int group = Hq / Hkv;
     plan.n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
-    plan.nsplit = decode_nsplit(B, Hq, Hkv, S);
+    plan.nsplit = decode_nsplit(B, Hq, Hkv, S, d);
     const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
     auto cum = [&](int64_t c) { return decode_prefix_bytes(std::min(S, c * kKeyTile), S, P, d, Wi); };
     const double total = cum(nchunks);
@@ -602,7 +605,7 @@ atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool,
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
     a.n_slabs = (a.group + kDecodeHeads - 1) / kDecodeHeads;
-    paged_plan(Hq, Hkv, max_len, a.split_budget, a.nsplit);
+    paged_plan(Hq, Hkv, max_len, d, a.split_budget, a.nsplit);
     if (launch_decode_paged_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
     return read_counter(a.counter, skipped_out, s);
 }
