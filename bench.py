@@ -40,6 +40,8 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_counters.
 DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kv262144_counters.txt")
 KCACHE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kcache_kv262144_counters.txt")
 PAGED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_paged_kv262144_counters.txt")
+GPTJ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gptj_kv262144_counters.txt")
+D256_DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_d256_kv65536_counters.txt")
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
@@ -174,7 +176,8 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     gbs = nbytes / (ms * 1e-3) / 1e9
     out["decode_gptj"] = {"value": gbs, "unit": "GB/s", "ms": ms, "config": dict(D, rope_layout="gptj"),
                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                                       "traffic": read_traffic(GPTJ_COUNTERS_FILE)}}
     log("decode (GPT-J layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (ms, gbs, 100 * gbs / HBM_PEAK_GBS))
     del q, k, v, o, ws
 
@@ -211,7 +214,8 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     gbs = nbytes / (ms * 1e-3) / 1e9
     out["decode_d256"] = {"value": gbs, "unit": "GB/s", "ms": ms, "config": D,
                           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes}}
+                                       "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                                       "traffic": read_traffic(D256_DECODE_COUNTERS_FILE)}}
     log("decode d=256 KV=%d: %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (D["S"], ms, gbs, 100 * gbs / HBM_PEAK_GBS))
     return out
 

@@ -140,6 +140,8 @@ atf_status atf_prefill_prepare_kv(const void *k, const void *v,
  * workspace prepared by atf_prefill_prepare_kv with the same B, Hkv, S, d,
  * rope_base, pos0 and dtype.  k and v are the raw inputs: the fp32 kernel
  * reads (and rotates) them directly; the bf16 kernel ignores them (NULL ok).
+ * One prepared workspace serves any number of calls (other q, alpha or
+ * causal); skipped_out counts the terms of this call only.
  */
 atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void *out,
                               int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d,

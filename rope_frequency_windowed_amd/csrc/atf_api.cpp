@@ -223,7 +223,9 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
-    hipError_t e;
+    // the count is per call: clear it (the prepared workspace may be reused)
+    hipError_t e = launch_fill_zero_u64(a.counter, s);
+    if (e != hipSuccess) return ATF_ERR_HIP;
     if (dtype == ATF_F32) {
         // the fp32 kernel rotates raw keys itself: `krot` carries k, `vt` carries v
         a.krot = k;

@@ -228,14 +228,18 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // ============================================================================
 // Prefill attention, bf16 in / fp32 accumulate, MFMA 32x32x16.
 //
-// Workgroup = 4 waves = 128 queries of one (b, h); wave w owns 32 queries.
-// Key tiles of 64 keys stream global -> LDS with direct LDS loads
+// Workgroup = 8 waves (two per SIMD) = 256 queries of one (b, h); wave w owns
+// 32 queries (d = 256: 4 waves, one per SIMD, 128 queries).  Key tiles of 128
+// keys (d = 256: 64) stream global -> LDS with direct LDS loads
 // (buffer_load_dwordx4 ... lds: no staging registers, the tile base advances
-// in scalar registers), double-buffered, one barrier per tile.  Per tile each wave computes two 32x32 score blocks
-// S^T = K' Q'^T (keys on MFMA rows, queries on columns: a lane holds 16 keys
-// of one query, its partner lane^32 the other 16, so softmax row statistics
-// need one lane swap), then O^T += V^T P^T.  Both blocks' score MFMAs are
-// issued before the first block's softmax so the VALU work overlaps them.
+// in scalar registers), double-buffered, one barrier per tile.  Per 32-key
+// block each wave computes a 32x32 score block S^T = K' Q'^T (keys on MFMA
+// rows, queries on columns: a lane holds 16 keys of one query, its partner
+// lane^32 the other 16, so softmax row statistics need one lane swap), then
+// O^T += V^T P^T.  Blocks go in pairs, chain0 | chain1 + probs0 | PV0 +
+// probs1 | PV1, so the exponentials sit beside MFMA runs.  Tiles where every
+// key precedes every query of the wave and no window falls inside the tile's
+// distance range take a fast path with one pair cut for all their blocks.
 //
 // Windows per 32x32 block: distances span [dmin, dmax]; pairs below
 // p_lo = p*(dmin) are dropped everywhere in the block, pairs from

@@ -180,3 +180,24 @@ def test_bf16_workload_sizes_sampled(env, S, alpha, per_head, heads):
     dense, _ = oracle.attention(qrows, kk, vv, base=base, alpha=math.inf, rows=rows, q_shape=(B, Hq, S, d))
     log("  kv heads %s, %d rows" % (heads_kv, len(rows)))
     check_bf16(got, ref, dense, "S=%d alpha=%g" % (S, alpha))
+
+
+@pytest.mark.parametrize("dtype_name", ["bfloat16", "float32"])
+def test_prepared_workspace_reused(env, dtype_name):
+    """One prepare, several attend calls with different alpha: each call's
+    count is its own (the counter is cleared per call) and each output
+    matches a fresh atf_prefill."""
+    torch, oracle, atf, inputs = env
+    dtype = getattr(torch, dtype_name)
+    B, Hq, Hkv, S, d = 1, 4, 2, 700, 128 if dtype_name == "bfloat16" else 64
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, S, d, dtype=dtype, device=torch.device("cuda:0"))
+    code = atf.ATF_BF16 if dtype_name == "bfloat16" else atf.ATF_F32
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(B, Hkv, S, d, code), dtype=torch.uint8, device=q.device)
+    atf.atf_prefill_prepare_kv(k, v, rope_base=1e6, ws=ws)
+    for alpha in (0.5, 1.0, 2.0, 1.0):
+        out = torch.empty_like(q)
+        got = atf.atf_prefill_attend(q, k, v, out, rope_base=1e6, alpha=alpha, ws=ws, return_skipped=True)
+        assert got == B * Hq * atf.atf_skipped_pair_products(S, d, 1e6, alpha, 1, 0)
+        fresh = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=alpha)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fresh)
