@@ -245,6 +245,20 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    # attainable peaks on this GPU (microbenchmarks), beside the published ones
+    from rope_frequency_windowed_amd import probes
+    attainable = {"mfma_bf16_tflops": probes.mfma_bf16_tflops(torch, dev),
+                  "hbm_read_gbs": probes.hbm_read_gbs(torch, dev)}
+    log("attainable: %.0f TFLOP/s dense bf16 MFMA, %.0f GB/s HBM read"
+        % (attainable["mfma_bf16_tflops"], attainable["hbm_read_gbs"]))
+
+    def attain(roof):
+        """Adds the measured peak and the fraction of it to a roofline dict."""
+        key = "mfma_bf16_tflops" if roof["bound"] == "mfma" else "hbm_read_gbs"
+        roof["attainable_peak"] = attainable[key]
+        roof["frac_of_attainable"] = roof["achieved"] / attainable[key]
+        return roof
+
     do_prefill = args.only in (None, "prefill")
     do_decode = args.only in (None, "decode")
     do_kcache = args.only in (None, "kcache")
@@ -356,10 +370,10 @@ def main():
         achieved = flops / (attend_ms * 1e-3) / 1e12
         res["value"] = PREFILL["B"] * PREFILL["S"] / (prefill_ms * 1e-3)
         res["unit"] = "tok/s"
-        res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                           "traffic": read_traffic(), "kernel": "prefill_bf16_kernel<128>",
-                           "kernel_ms": attend_ms, "algorithmic_flops_per_launch": flops}
+        res["roofline"] = attain({"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                                  "traffic": read_traffic(), "kernel": "prefill_bf16_kernel<128>",
+                                  "kernel_ms": attend_ms, "algorithmic_flops_per_launch": flops})
         config["prefill"] = dict(PREFILL, prep_ms=prep_ms, attend_ms=attend_ms)
         log("prefill: prep %.3f ms, attend %.3f ms, %.1f TFLOP/s algorithmic (%.1f%% of bf16 peak), %.0f tok/s"
             % (prep_ms, attend_ms, achieved, 100 * achieved / MFMA_BF16_PEAK_TFLOPS, res["value"]))
@@ -368,9 +382,10 @@ def main():
         nbytes = decode_algorithmic_bytes(atf, **DECODE)
         gbs = nbytes / (dec_ms * 1e-3) / 1e9
         res["decode"] = {"value": gbs, "unit": "GB/s", "ms": dec_ms, "tok_per_s": DECODE["B"] / (dec_ms * 1e-3),
-                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
-                                      "traffic": read_traffic(DECODE_COUNTERS_FILE)}}
+                         "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                             "algorithmic_bytes_per_launch": nbytes,
+                                             "traffic": read_traffic(DECODE_COUNTERS_FILE)})}
         config["decode"] = dict(DECODE)
         log("decode: %.3f ms, %.3g algorithmic bytes, %.0f GB/s (%.1f%% of HBM peak)"
             % (dec_ms, nbytes, gbs, 100 * gbs / HBM_PEAK_GBS))
@@ -383,9 +398,9 @@ def main():
         res["decode_kcache"] = {
             "value": gbs, "unit": "GB/s", "ms": kc_ms, "tok_per_s": DECODE["B"] / (kc_ms * 1e-3),
             "layout": "rotated keys in 64-key blocks of 4-pair planes (atf_decode_pack_k)",
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
-                         "traffic": read_traffic(KCACHE_COUNTERS_FILE)}}
+            "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                                "traffic": read_traffic(KCACHE_COUNTERS_FILE)})}
         log("decode (key-cache layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
             % (kc_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
         if not do_prefill and not do_decode:
@@ -397,17 +412,21 @@ def main():
         res["decode_paged"] = {
             "value": gbs, "unit": "GB/s", "ms": pg_ms, "tok_per_s": DECODE["B"] / (pg_ms * 1e-3),
             "layout": "key-cache layout in 64-token pages, seeded random page table, lengths on the device",
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
-                         "traffic": read_traffic(PAGED_COUNTERS_FILE)}}
+            "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                                "traffic": read_traffic(PAGED_COUNTERS_FILE)})}
         log("decode (paged key cache): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
             % (pg_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
         if args.only == "paged":
             res["value"], res["unit"] = gbs, "GB/s"
     if do_variants:
         res["variants"] = variant_legs(atf, torch, make_qkv, dev, stream, args.steps)
+        for leg in res["variants"].values():
+            attain(leg["roofline"])
         if args.only == "variants":
             res["value"], res["unit"] = res["variants"]["decode_gptj"]["value"], "GB/s"
+    res["attainable"] = dict(attainable, note="this GPU, microbenchmarks in librfw_probes.so: 8 independent "
+                             "32x32x16 bf16 MFMA chains per wave; one pass over an 8 GiB buffer in 16-byte loads")
     res["config"] = config
     if do_prefill and not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(q, k, v, PREFILL)

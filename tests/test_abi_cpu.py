@@ -296,3 +296,20 @@ def _call_pdecode(lib, **kw):
 ])
 def test_paged_decode_rejects(lib, kw, expect):
     assert _call_pdecode(lib, **kw) == expect
+
+
+def test_probe_library_exports_and_checks_arguments():
+    """The microbenchmark library exports what include/atf_probes.h declares
+    and rejects bad arguments on the host (nothing is launched)."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "include", "atf_probes.h")).read()
+    names = set(re.findall(r"^int (atf_probe_\w+)\(", hdr, re.M))
+    assert names == {"atf_probe_mfma_bf16", "atf_probe_hbm_read"}
+    from rope_frequency_windowed_amd import probes
+    lib = probes.library()
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.atf_probe_mfma_bf16(None, None, 1, 1, None) == 1
+    assert lib.atf_probe_mfma_bf16(16, 32, 0, 1, None) == 1
+    assert lib.atf_probe_hbm_read(16, 100, 32, 1, None) == 1      # size not a multiple of 256 KiB
+    assert lib.atf_probe_hbm_read(8, 1 << 18, 32, 1, None) == 1   # misaligned
