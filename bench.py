@@ -147,6 +147,14 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_each_way": n, "launches": 5}))
 
 
+def leg_stats(times):
+    """mean, median and min of per-step times (ms)."""
+    t = sorted(times)
+    n = len(t)
+    med = t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+    return sum(t) / n, med, t[0]
+
+
 def time_leg(torch, stream, fn, steps):
     """Average ms of fn() over `steps` calls (one untimed call first), HIP events
     on the library's stream."""
@@ -163,7 +171,8 @@ def time_leg(torch, stream, fn, steps):
 
 def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     """Decode at the main decode size with GPT-J interleaved pairs (standard
-    [S][d] cache), and prefill/decode with 256-dim heads."""
+    [S][d] cache); prefill at S=32K, at 128K with alpha 0.5 and 2, and at 1M;
+    prefill/decode with 256-dim heads."""
     out = {}
     D = DECODE
     q, k, v = make_qkv(D["B"], D["Hq"], D["Hkv"], 1, D["S"], D["d"], dtype=torch.bfloat16, device=dev)
@@ -180,6 +189,29 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
                                        "traffic": read_traffic(GPTJ_COUNTERS_FILE)}}
     log("decode (GPT-J layout): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)" % (ms, gbs, 100 * gbs / HBM_PEAK_GBS))
     del q, k, v, o, ws
+
+    # the other prefill workloads: S=32K, 128K at alpha 0.5 and 2, and 1M (one rep)
+    for S, alpha, reps in ((32768, 1.0, steps), (131072, 0.5, 3), (131072, 2.0, 3), (1 << 20, 1.0, 1)):
+        P = dict(PREFILL, S=S, alpha=alpha)
+        q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], S, S, P["d"], dtype=torch.bfloat16, device=dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], S, P["d"], atf.ATF_BF16),
+                         dtype=torch.uint8, device=dev)
+        atf.atf_prefill_prepare_kv(k, v, rope_base=P["base"], ws=ws)
+        got = atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=alpha, ws=ws, return_skipped=True)
+        if got != P["B"] * P["Hq"] * atf.atf_skipped_pair_products(S, P["d"], P["base"], alpha):
+            raise SystemExit("prefill S=%d alpha=%g dropped-term count differs from the closed form" % (S, alpha))
+        ms = time_leg(torch, stream, lambda: atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=alpha,
+                                                                    ws=ws), reps)
+        flops = prefill_algorithmic_flops(atf, **P)
+        tf = flops / (ms * 1e-3) / 1e12
+        out["prefill_s%d_alpha%g" % (S, alpha)] = {
+            "value": P["B"] * S / (ms * 1e-3), "unit": "tok/s (attention kernel)", "ms": ms, "config": P,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops}}
+        log("prefill S=%d alpha=%g: attend %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
+            % (S, alpha, ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+        del q, k, v, o, ws
 
     P = PREFILL_D256
     q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], P["S"], P["S"], P["d"], dtype=torch.bfloat16, device=dev)
@@ -312,6 +344,17 @@ def main():
         plens = torch.full((D["B"],), D["S"], dtype=torch.int32, device=dev)
         pws = torch.empty(atf.atf_decode_paged_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
                           dtype=torch.uint8, device=dev)
+    # decode legs start from cold caches: one read pass over a 512 MB buffer
+    # before each (outside their timed events; larger than the 256 MB last-level
+    # cache, and a read leaves no dirty lines for the decode to write back)
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev) if (do_decode or do_kcache or do_paged) else None
+    flush_sink = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
+
+    def cold():
+        if probes.library().atf_probe_hbm_read(flush.data_ptr(), flush.numel(), flush_sink.data_ptr(), 4096,
+                                               stream.cuda_stream) != 0:
+            raise SystemExit("cache flush failed")
+
     torch.cuda.synchronize()
 
     def step(ev=None):
@@ -325,12 +368,14 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
         if do_decode:
+            cold()
             if ev is not None:
                 ev[3].record(stream)
             atf.atf_decode(dq, dk, dv, dout, rope_base=D["base"], alpha=D["alpha"], ws=dws)
             if ev is not None:
                 ev[4].record(stream)
         if do_kcache:
+            cold()
             if ev is not None:
                 ev[5].record(stream)
             atf.atf_decode_kcache(kq, kcache, kv, kout, S=DECODE["S"], rope_base=DECODE["base"],
@@ -338,6 +383,7 @@ def main():
             if ev is not None:
                 ev[6].record(stream)
         if do_paged:
+            cold()
             if ev is not None:
                 ev[7].record(stream)
             atf.atf_decode_paged(pq, kpool, vpool, ptab, plens, pout, max_len=DECODE["S"], rope_base=DECODE["base"],
@@ -364,7 +410,7 @@ def main():
                           "d=128, RoPE base 1e6, alpha=1), iid N(0,1) seeds 1000/1001/1002"}
     if do_prefill:
         prep_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-        attend_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+        attend_ms, attend_med, attend_min = leg_stats([e[1].elapsed_time(e[2]) for e in events])
         prefill_ms = prep_ms + attend_ms
         flops = prefill_algorithmic_flops(atf, **PREFILL)
         achieved = flops / (attend_ms * 1e-3) / 1e12
@@ -374,14 +420,17 @@ def main():
                                   "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                                   "traffic": read_traffic(), "kernel": "prefill_bf16_kernel<128>",
                                   "kernel_ms": attend_ms, "algorithmic_flops_per_launch": flops})
-        config["prefill"] = dict(PREFILL, prep_ms=prep_ms, attend_ms=attend_ms)
+        config["prefill"] = dict(PREFILL, prep_ms=prep_ms, attend_ms=attend_ms, attend_ms_median=attend_med,
+                                 attend_ms_min=attend_min,
+                                 exp_count=PREFILL["B"] * PREFILL["Hq"] * PREFILL["S"] * (PREFILL["S"] + 1) // 2)
         log("prefill: prep %.3f ms, attend %.3f ms, %.1f TFLOP/s algorithmic (%.1f%% of bf16 peak), %.0f tok/s"
             % (prep_ms, attend_ms, achieved, 100 * achieved / MFMA_BF16_PEAK_TFLOPS, res["value"]))
     if do_decode:
-        dec_ms = sum(e[3].elapsed_time(e[4]) for e in events) / args.steps
+        dec_ms, dec_med, dec_min = leg_stats([e[3].elapsed_time(e[4]) for e in events])
         nbytes = decode_algorithmic_bytes(atf, **DECODE)
         gbs = nbytes / (dec_ms * 1e-3) / 1e9
-        res["decode"] = {"value": gbs, "unit": "GB/s", "ms": dec_ms, "tok_per_s": DECODE["B"] / (dec_ms * 1e-3),
+        res["decode"] = {"value": gbs, "unit": "GB/s", "ms": dec_ms, "ms_median": dec_med, "ms_min": dec_min,
+                         "tok_per_s": DECODE["B"] / (dec_ms * 1e-3),
                          "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                              "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                              "algorithmic_bytes_per_launch": nbytes,
@@ -392,11 +441,12 @@ def main():
         if not do_prefill:
             res["value"], res["unit"] = gbs, "GB/s"
     if do_kcache:
-        kc_ms = sum(e[5].elapsed_time(e[6]) for e in events) / args.steps
+        kc_ms, kc_med, kc_min = leg_stats([e[5].elapsed_time(e[6]) for e in events])
         nbytes = decode_algorithmic_bytes(atf, **DECODE)
         gbs = nbytes / (kc_ms * 1e-3) / 1e9
         res["decode_kcache"] = {
-            "value": gbs, "unit": "GB/s", "ms": kc_ms, "tok_per_s": DECODE["B"] / (kc_ms * 1e-3),
+            "value": gbs, "unit": "GB/s", "ms": kc_ms, "ms_median": kc_med, "ms_min": kc_min,
+            "tok_per_s": DECODE["B"] / (kc_ms * 1e-3),
             "layout": "rotated keys in 64-key blocks of 4-pair planes (atf_decode_pack_k)",
             "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
@@ -406,11 +456,12 @@ def main():
         if not do_prefill and not do_decode:
             res["value"], res["unit"] = gbs, "GB/s"
     if do_paged:
-        pg_ms = sum(e[7].elapsed_time(e[8]) for e in events) / args.steps
+        pg_ms, pg_med, pg_min = leg_stats([e[7].elapsed_time(e[8]) for e in events])
         nbytes = decode_algorithmic_bytes(atf, **DECODE)
         gbs = nbytes / (pg_ms * 1e-3) / 1e9
         res["decode_paged"] = {
-            "value": gbs, "unit": "GB/s", "ms": pg_ms, "tok_per_s": DECODE["B"] / (pg_ms * 1e-3),
+            "value": gbs, "unit": "GB/s", "ms": pg_ms, "ms_median": pg_med, "ms_min": pg_min,
+            "tok_per_s": DECODE["B"] / (pg_ms * 1e-3),
             "layout": "key-cache layout in 64-token pages, seeded random page table, lengths on the device",
             "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
