@@ -96,3 +96,17 @@ def test_decode_workload_full(env):
     dense, _ = oracle.attention(q, k, v, base=1e6, alpha=math.inf, q_pos0=262144, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, dense, "decode 256K")
     assert skipped == ref_skipped == 8 * 28 * atf.atf_skipped_pair_products(262144, 128, 1e6, 1.0, 1, 1)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,d", [(2, 4, 4, 3000, 128),     # plain multi-head (group 1)
+                                          (1, 64, 1, 2000, 64),     # the largest group: 8 slabs of 8 heads
+                                          (16, 8, 2, 700, 128)])    # many sequences
+def test_decode_group_and_batch_edges(env, B, Hq, Hkv, S, d):
+    torch, oracle, atf, inputs = env
+    log("case: decode edges %s" % ((B, Hq, Hkv, S, d),))
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, 1, S, d, dtype=torch.bfloat16, device=torch.device("cuda:0"))
+    out, skipped = atf.atf_decode(q, k, v, rope_base=1e4, alpha=1.0, return_skipped=True)
+    torch.cuda.synchronize()
+    ref, ref_skipped = oracle.attention(q, k, v, base=1e4, alpha=1.0, q_pos0=S, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "decode edges")
+    assert skipped == ref_skipped

@@ -201,3 +201,17 @@ def test_prepared_workspace_reused(env, dtype_name):
         fresh = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=alpha)
         torch.cuda.synchronize()
         assert torch.equal(out, fresh)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,d", [(1, 4, 4, 700, 128),      # plain multi-head (group 1)
+                                          (1, 64, 1, 300, 64),      # the largest supported group
+                                          (4, 8, 2, 257, 128)])     # a batch of sequences
+def test_prefill_group_and_batch_edges(env, B, Hq, Hkv, S, d):
+    torch, oracle, atf, inputs = env
+    log("case: prefill edges %s" % ((B, Hq, Hkv, S, d),))
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, S, S, d, dtype=torch.bfloat16, device=torch.device("cuda:0"))
+    out, skipped = atf.atf_prefill(q, k, v, rope_base=1e4, alpha=1.0, return_skipped=True)
+    torch.cuda.synchronize()
+    ref, ref_skipped = oracle.attention(q, k, v, base=1e4, alpha=1.0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "prefill edges")
+    assert skipped == ref_skipped
