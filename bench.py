@@ -16,6 +16,7 @@ against their roofline; `cpu_baseline` is the fp64 oracle timed on a bounded
 sample on the host.
 
   python bench.py [--steps K] [--warmup W] [--only prefill|decode|kcache|paged|variants] [--no-cpu]
+                  [--no-variants]
   python bench.py --copy-probe      (plain copy kernel of known size, for the
                                      HBM-counter scale factor)
 """
@@ -259,6 +260,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--only", choices=["prefill", "decode", "kcache", "paged", "variants"], default=None)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="main step only (prefill 128K + the decode legs)")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
 
@@ -295,7 +297,7 @@ def main():
     do_decode = args.only in (None, "decode")
     do_kcache = args.only in (None, "kcache")
     do_paged = args.only in (None, "paged")
-    do_variants = args.only in (None, "variants")
+    do_variants = args.only in (None, "variants") and not args.no_variants
 
     if do_prefill:
         P = PREFILL
