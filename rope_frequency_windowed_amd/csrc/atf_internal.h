@@ -15,14 +15,17 @@ constexpr int kKeyTile = 64;      // keys per prefill tile / decode chunk
 #ifndef ATF_PREFILL_KEYS
 #define ATF_PREFILL_KEYS 128
 #endif
-constexpr int kPrefillWaves = ATF_PREFILL_WAVES;       // waves per prefill workgroup (bf16)
-constexpr int kPrefillKeys = ATF_PREFILL_KEYS;         // keys per prefill LDS tile (bf16)
-// d = 256: a wave's query fragments and output accumulators need one wave per
-// SIMD (512 registers), so 4-wave workgroups; 64-key tiles keep the double
-// buffer at 128 KB of LDS.
-constexpr int prefill_waves(int d) { return d == 256 ? 4 : kPrefillWaves; }
-constexpr int prefill_keys(int d) { return d == 256 ? 64 : kPrefillKeys; }
-constexpr int prefill_query_tile(int d) { return 32 * prefill_waves(d); }  // queries per workgroup (bf16)
+// bf16 prefill, d <= 128: MFMA 32x32x16, 32 queries per wave
+constexpr int kPrefillWaves = ATF_PREFILL_WAVES;       // waves per workgroup
+constexpr int kPrefillKeys = ATF_PREFILL_KEYS;         // keys per LDS tile
+// bf16 prefill, d = 256: MFMA 16x16x32, 16 queries per wave.  With 32 queries
+// a wave's query fragments and accumulators would need one wave per SIMD; 16
+// queries fit two per SIMD.  64-key tiles keep the double buffer at 128 KB.
+constexpr int kPrefill16Waves = 8;
+constexpr int kPrefill16Keys = 64;
+constexpr int prefill_query_tile(int d) {  // queries per workgroup (bf16)
+    return d == 256 ? 16 * kPrefill16Waves : 32 * kPrefillWaves;
+}
 constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
 constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
 constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves

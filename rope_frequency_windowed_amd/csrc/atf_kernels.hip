@@ -228,9 +228,9 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // ============================================================================
 // Prefill attention, bf16 in / fp32 accumulate, MFMA 32x32x16.
 //
+// d <= 128 (d = 256 runs on prefill16_bf16_kernel below).
 // Workgroup = 8 waves (two per SIMD) = 256 queries of one (b, h); wave w owns
-// 32 queries (d = 256: 4 waves, one per SIMD, 128 queries).  Key tiles of 128
-// keys (d = 256: 64) stream global -> LDS with direct LDS loads
+// 32 queries.  Key tiles of 128 keys stream global -> LDS with direct LDS loads
 // (buffer_load_dwordx4 ... lds: no staging registers, the tile base advances
 // in scalar registers), double-buffered, one barrier per tile.  Per 32-key
 // block each wave computes a 32x32 score block S^T = K' Q'^T (keys on MFMA
@@ -256,6 +256,23 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // q' is pre-scaled by log2(e)/sqrt(d), and each score chain starts with a
 // rank-1 MFMA that puts -m_ref in every element, so a probability is 2^score.
 // ============================================================================
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ inline float quad_max(float x) {  // max over lanes t, t+16, t+32, t+48
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1]));
+}
+__device__ inline float quad_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+}
 
 __device__ inline float partner_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -438,11 +455,11 @@ __device__ inline void qk_pair(int s_first, const unsigned char *lds, unsigned k
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(prefill_waves(D) * 64, D == 256 ? 1 : 8 / kPrefillWaves) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill_bf16_kernel(
     AttnArgs a) {
     constexpr int P = D / 2;
-    constexpr int NW = prefill_waves(D);  // waves per workgroup (two per SIMD; one at d = 256)
-    constexpr int KT = prefill_keys(D);   // keys per LDS tile
+    constexpr int NW = kPrefillWaves;  // waves per workgroup (two per SIMD)
+    constexpr int KT = kPrefillKeys;   // keys per LDS tile
     constexpr int QT = 32 * NW;           // queries per workgroup
     constexpr int NB = KT / 32;        // 32-key score blocks per tile
     constexpr int NSTEP = D / 16;      // MFMA K-steps of 16 dims (8 pairs)
@@ -452,6 +469,7 @@ __global__ __launch_bounds__(prefill_waves(D) * 64, D == 256 ? 1 : 8 / kPrefillW
     constexpr unsigned TILE_BYTES = 2 * KT_BYTES;  // K' then V^T (KT/64 tiles of [D][64])
     constexpr int NLD = KT_BYTES / 1024 / NW;      // 1 KB direct loads per wave per tile (each of K', V^T)
     static_assert(NLD >= 1 && NB % 2 == 0, "tile shape");
+    static_assert(D <= 128, "d = 256 has its own kernel");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
 
     // ---- work item: longest query tiles first; the group heads sharing one kv
@@ -522,12 +540,13 @@ __global__ __launch_bounds__(prefill_waves(D) * 64, D == 256 ? 1 : 8 / kPrefillW
     // (c_min: first 16-byte chunk any wave reads in this tile).
     // Piece n of wave w is tile piece n*NW + w.  When the piece stride covers
     // whole swizzle periods every piece of a lane has the same swizzle (one
-    // per-lane offset plus n * NW KB in a scalar); otherwise (d = 256) the lane
-    // has KPER offsets, piece n using offset n % KPER.
+    // per-lane offset plus n * NW KB in a scalar); otherwise the lane has KPER
+    // offsets, piece n using offset n % KPER.
     constexpr int KPERIOD = CH * 16 * kswz_rows<CH>();  // bytes of one key-swizzle period
     constexpr int KPER = (KPERIOD > NW * 1024) ? KPERIOD / (NW * 1024) : 1;
     static_assert((NW * 1024) % KPERIOD == 0 || KPERIOD % (NW * 1024) == 0, "piece stride vs key swizzle");
-    static_assert((NW * 1024) % (128 * 8) == 0, "a piece stride must keep the value-row swizzle");
+    // swz8 repeats every 16 value rows (2 KB)
+    static_assert((NW * 1024) % (128 * 16) == 0, "a piece stride must keep the value-row swizzle");
     unsigned k_goff[KPER], v_goff;
     int k_chunk[KPER];
 #pragma unroll
@@ -808,6 +827,385 @@ __global__ __launch_bounds__(prefill_waves(D) * 64, D == 256 ? 1 : 8 / kPrefillW
 }
 
 // ============================================================================
+// Prefill attention, bf16 in / fp32 accumulate, MFMA 16x16x32: the d = 256
+// kernel (written for d = 128 or 256; at d = 128 the 32x32 kernel above is
+// faster, since here P.V reads V^T from LDS at twice the rate per flop).
+//
+// Workgroup = 8 waves (two per SIMD) = 128 queries of one (b, h); wave w owns
+// 16 queries, so its accumulators (16 x 256 fp32) and query fragments fit two
+// waves per SIMD.  Key tiles (64 keys at d = 256) stream into LDS with direct
+// loads from the same prepared K' / V^T as the 32x32 kernel, double-buffered,
+// one barrier per tile.  Per 32-key block a wave computes two 16x16 score
+// blocks S^T = K' Q'^T (sub-block sb: MFMA row t is key 2(t & 8) + (t & 7) +
+// 8 sb of the block) over the kept 32-dim K-steps (16 pairs each), then
+// O^T[16 dims x 16 queries] += V^T P^T for every 16-dim output block.  Lane
+// (t, g) = (lane % 16, lane / 16) owns query t; its score rows 4g + r (r =
+// 0..3) of sub-block sb are key 16(g >> 1) + 4(g & 1) + 8 sb + r, exactly
+// the keys the value tile's in-group permutation puts in that lane's P.V
+// operand, so the four probability words are the operand as they stand.
+//
+// Windows, fast tiles, boundary pairs, masks and counting follow the 32x32
+// kernel, on 16-pair K-steps: pairs below the cut inside the first kept step
+// are zeroed on the query side (once per tile on the fast path).  The softmax
+// reference enters as the initial accumulator: every element of a lane's
+// 16x16 score block belongs to its one query, so {-m_ref x 4} is the C
+// operand of the first score MFMA and a probability is 2^score.
+// ============================================================================
+
+// K' LDS swizzle of the 16x16 kernel: the 16 rows one 16-lane group reads
+// (keys 0..7 and 16..23 of a block, or 8..15 and 24..31) get 16 distinct
+// 16-byte bank groups, for 256- and 512-byte rows alike.
+__device__ inline int kswz_sub(int row) { return (row & 7) | (((row >> 4) & 1) << 3); }
+
+// keys of the lane's 8 score slots below x (slot (sb, r): key base_g + 8 sb + r)
+__device__ inline int slots_below16(int x, int base_g) {
+    return min(max(x - base_g, 0), 4) + min(max(x - base_g - 8, 0), 4);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void prefill16_bf16_kernel(AttnArgs a) {
+    constexpr int P = D / 2;
+    constexpr int NW = kPrefill16Waves;
+    constexpr int KT = D == 256 ? kPrefill16Keys : 128;
+    constexpr int QT = 16 * NW;
+    constexpr int NB = KT / 32;
+    constexpr int NSTEP = D / 32;  // K-steps of 32 dims (16 pairs)
+    constexpr int CH = D / 8;      // 16-byte chunks per K' row
+    constexpr int NDB = D / 16;    // 16-dim output blocks
+    constexpr unsigned KT_BYTES = KT * D * 2;
+    constexpr unsigned TILE_BYTES = 2 * KT_BYTES;
+    constexpr int NPIECE = KT_BYTES / 1024;            // 1 KB pieces per tile (each of K', V^T)
+    constexpr int NLD = (NPIECE + NW - 1) / NW;        // pieces per wave
+    static_assert(D == 128 || D == 256, "16x16 prefill: d = 128 or 256");
+    static_assert(NW % 2 == 0, "swz8 repeats every 16 value rows (2 KB): the piece stride must keep it");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
+
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int gi = (slot / a.group) * 8 + xcd;
+    if (gi >= a.n_groups) return;
+    const int hg = slot % a.group;
+    const int per_qt = a.B * a.Hkv;
+    const int qt = a.n_qtiles - 1 - gi / per_qt;
+    const int rem = gi % per_qt;
+    const int b = rem / a.Hkv, hk = rem % a.Hkv;
+    const int h = hk * a.group + hg;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int t = lane & 15, g = lane >> 4;
+    const int i0 = qt * QT + wave * 16;
+    const int my_q = i0 + t;
+    const bool q_valid = my_q < a.Sq;
+    const int qoff = (int)(a.q_pos0 - a.k_pos0);
+    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QT + qoff;
+    const WaveWin<P> win = load_windows<P>(a.W);
+    const int kbase_g = 16 * (g >> 1) + 4 * (g & 1);  // key of slot (sb 0, r 0) in a block
+
+    // query operand: step s holds pairs 16 s + 4 g + (0..3) of query t, rotated and scaled
+    bf16x8_t qf[NSTEP];
+    {
+        const unsigned short *qrow = (const unsigned short *)a.q + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+        const long long pos = a.q_pos0 + my_q;
+        const float sc = a.scale_log2;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+            if (q_valid) {
+                const int p0 = 16 * s + 4 * g;
+                u32x2 lo, hi;
+                load_pair_pieces(qrow, p0, P, a.gptj != 0, lo, hi);
+                unsigned r[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float x, y, c, sn;
+                    pair_xy(lo, hi, u, a.gptj != 0, x, y);
+                    rope_cos_sin(pos, a.theta[p0 + u], c, sn);
+                    r[u] = pack_bf((x * c - y * sn) * sc, (y * c + x * sn) * sc);
+                }
+                w = (u32x4){r[0], r[1], r[2], r[3]};
+            }
+            qf[s] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    }
+
+    const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
+    const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
+    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
+    const int n_kt = last_key / KT + 1;
+
+    // Tile loader: piece m (1 KB) of K' lands lane-linear at LDS byte 1024 m +
+    // 16 l, i.e. row (1024 m + 16 l) / row_bytes, physical chunk l % CH; the
+    // lane fetches the logical chunk the swizzle maps there (chunks below
+    // c_min, whose pairs the whole workgroup drops, read past the buffer end
+    // and land as zeros).  V^T pieces keep one per-lane offset: the piece
+    // stride NW KB is a whole number of value-swizzle periods.
+    unsigned v_goff;
+    {
+        const int kbyte = wave * 1024 + lane * 16;
+        const int vrow = kbyte / 128;
+        v_goff = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
+    }
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+#define ATF16_TILE_LOAD(kt_, buf_)                                                           \
+    {                                                                                      \
+        const int j0_ = (kt_) * KT;                                                        \
+        const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
+                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QT - 1))); \
+        const int c_min_ = cut_below(win, dmin_wg_) >> 2;                                  \
+        const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
+        const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
+        unsigned char *lk_ = lds + (buf_) * TILE_BYTES;                                    \
+        _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
+            const int m_ = n * NW + wave_s;                                                \
+            if (NPIECE % NW == 0 || m_ < NPIECE) {                                         \
+                const int krow_ = (1024 * m_ + 16 * lane) / (CH * 16);                     \
+                const int kch_ = (lane % CH) ^ kswz_sub(krow_);                               \
+                const unsigned koff_ = kch_ >= c_min_ ? (unsigned)(kch_ * 16 + (lane / CH) * (CH * 16)) : KT_BYTES; \
+                lds_dma16_buf(kr_, koff_, m_ * 1024, lk_ + m_ * 1024);                     \
+                lds_dma16_buf(vr_, v_goff, n * NW * 1024, lk_ + KT_BYTES + wave_s * 1024 + n * NW * 1024); \
+            }                                                                              \
+        }                                                                                  \
+    }
+
+    f32x4_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    constexpr float kSumLimit = 4096.f;
+    constexpr unsigned kOnes = 0x3f803f80u;
+    float m_ref = 0.f, l_run = 0.f;
+    bool first = true;
+    // -m_ref in every element: the first score MFMA of a block starts from it,
+    // so scores leave the chain shifted by the reference (a lane's 4 elements
+    // all belong to its query t)
+    f32x4_t negm = {0.f, 0.f, 0.f, 0.f};
+    unsigned long long skipped = 0, skipped_u = 0;
+    unsigned fast_cut = 0;
+    const unsigned nq = (unsigned)__builtin_popcountll(__ballot(q_valid && g == 0));
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    // per-lane LDS byte offsets: K' row of MFMA row t in sub-block sb of block
+    // kb is 32 kb + 2(t & 8) + (t & 7) + 8 sb; V^T row of output block db is 16 db + t
+    const int krow_t = 2 * (t & 8) + (t & 7);
+    const unsigned ksw0 = (unsigned)kswz_sub(krow_t), ksw1 = (unsigned)kswz_sub(krow_t + 8);
+    const unsigned vrow_base = KT_BYTES + (unsigned)t * 128;
+
+    ATF16_TILE_LOAD(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < n_kt) ATF16_TILE_LOAD(kt + 1, buf ^ 1);
+        const unsigned char *lt = lds + buf * TILE_BYTES;
+        const int j0 = kt * KT;
+
+        // key fragment of step s, sub-block sb, block kb (chunk 4 s + g)
+        auto kfrag = [&](int kb, int sb, int s) -> u32x4 {
+            const unsigned row = 32u * kb + krow_t + 8u * sb;
+            const unsigned sw = sb ? ksw1 : ksw0;
+            return *(const u32x4 *)(lt + row * (CH * 16) + (((unsigned)(4 * s + g) ^ sw) << 4));
+        };
+        // query operand of step s0 with the lane's pairs below the cut zeroed
+        auto qmask = [&](int s0, int zb) -> bf16x8_t {
+            bf16x8_t qv = qf[0];
+#pragma unroll
+            for (int ss = 1; ss < NSTEP; ++ss) qv = (s0 == ss) ? qf[ss] : qv;
+            u32x4 w = __builtin_bit_cast(u32x4, qv);
+            w.x = (0 < zb) ? 0u : w.x;
+            w.y = (1 < zb) ? 0u : w.y;
+            w.z = (2 < zb) ? 0u : w.z;
+            w.w = (3 < zb) ? 0u : w.w;
+            return __builtin_bit_cast(bf16x8_t, w);
+        };
+        // scores of block kb over steps s0..NSTEP-1 (step s0 with the masked query qz)
+        auto scores = [&](int kb, int s0, bf16x8_t qz, f32x4_t &c0, f32x4_t &c1) {
+            c0 = negm;
+            c1 = negm;
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s) {
+                if (s < s0) continue;
+                const u32x4 k0 = kfrag(kb, 0, s), k1 = kfrag(kb, 1, s);
+                const bf16x8_t qs = (s == s0) ? qz : qf[s];
+                c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qs, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qs, c1, 0, 0, 0);
+            }
+        };
+        auto probs = [&](const f32x4_t &c0, const f32x4_t &c1, u32x4 &pw, float &ls) {
+            pw.x = pack_bf(fast_exp2(c0[0]), fast_exp2(c0[1]));
+            pw.y = pack_bf(fast_exp2(c0[2]), fast_exp2(c0[3]));
+            pw.z = pack_bf(fast_exp2(c1[0]), fast_exp2(c1[1]));
+            pw.w = pack_bf(fast_exp2(c1[2]), fast_exp2(c1[3]));
+            ls = dot2_bf(pw.x, kOnes, 0.f);
+            ls = dot2_bf(pw.y, kOnes, ls);
+            ls = dot2_bf(pw.z, kOnes, ls);
+            ls = dot2_bf(pw.w, kOnes, ls);
+        };
+        // move the reference when a lane's block sum overflows (or at the first block)
+        auto rescale = [&](f32x4_t &c0, f32x4_t &c1, u32x4 &pw, float &ls) {
+            if (__ballot(first || !(ls <= kSumLimit))) {
+                float bm = fmaxf(fmaxf(fmaxf(c0[0], c0[1]), fmaxf(c0[2], c0[3])),
+                                 fmaxf(fmaxf(c1[0], c1[1]), fmaxf(c1[2], c1[3])));
+                bm = quad_max(bm);  // block max relative to m_ref
+                const float m_new = first ? m_ref + bm : fmaxf(m_ref, m_ref + bm);
+                const float shift = m_new - m_ref;
+                if (!first) {
+                    const float corr = fast_exp2(-shift);
+                    l_run *= corr;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) o[db] *= corr;
+                }
+                m_ref = m_new;
+                negm = (f32x4_t){-m_ref, -m_ref, -m_ref, -m_ref};
+                c0 -= shift;
+                c1 -= shift;
+                probs(c0, c1, pw, ls);
+            }
+            first = false;
+            l_run += ls;
+        };
+        auto pv = [&](int kb, const u32x4 &pw) {
+            const unsigned char *lv = lt + (kb >> 1) * (D * 128);
+            const unsigned ch = (unsigned)(4 * (kb & 1) + g);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const unsigned row = 16u * db + (unsigned)t;
+                const u32x4 vf = *(const u32x4 *)(lv + vrow_base + 16u * db * 128 + ((ch ^ (unsigned)swz8((int)row)) << 4));
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                                __builtin_bit_cast(bf16x8_t, pw), o[db], 0, 0, 0);
+            }
+        };
+
+        bool fast;
+        int p_t;
+        {
+            const int jl = j0 + KT - 1;
+            if (CAUSAL) {
+                fast = jl <= i0k;
+                p_t = cut_below(win, i0k + 15 - j0);
+                fast = fast && cut_below(win, i0k - jl) == p_t;
+            } else {
+                fast = false;
+                p_t = 0;
+            }
+        }
+        if (CAUSAL && fast) {
+            fast_cut += (unsigned)p_t;
+            const int sf = p_t >> 4, zb = p_t - 16 * sf - 4 * g;
+            const bf16x8_t qz = qmask(sf, zb);
+            auto tile = [&](auto s0c) {
+                constexpr int S0 = decltype(s0c)::value;
+#pragma unroll
+                for (int kb = 0; kb < NB; ++kb) {
+                    f32x4_t c0, c1;
+                    u32x4 pw;
+                    float ls;
+                    scores(kb, S0, qz, c0, c1);
+                    probs(c0, c1, pw, ls);
+                    rescale(c0, c1, pw, ls);
+                    pv(kb, pw);
+                }
+            };
+            // one case per K-step; the slowest pair is never cut, so sf < NSTEP
+#define ATF16_T(i) \
+                case i: if constexpr ((i) < NSTEP) tile(std::integral_constant<int, ((i) < NSTEP ? (i) : 0)>{}); break;
+            switch (min(sf, NSTEP - 1)) {
+                ATF16_T(0) ATF16_T(1) ATF16_T(2) ATF16_T(3) ATF16_T(4) ATF16_T(5) ATF16_T(6) ATF16_T(7)
+                default: break;
+            }
+#undef ATF16_T
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            continue;
+        }
+
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb) {
+            const int jb = j0 + 32 * kb;
+            const int dlo = i0k - jb - 31, dhi = i0k + 15 - jb;
+            const bool live = CAUSAL ? dhi >= 0 : jb < a.Sk;
+            if (!live) break;
+            const int amin = CAUSAL ? max(0, dlo) : max(0, max(dlo, -dhi));
+            const int amax = CAUSAL ? dhi : max(dhi, -dlo);
+            const int p_lo = cut_below(win, amin), p_full = cut_below(win, amax);
+            const bool diag = CAUSAL ? jb + 31 > i0k : jb + 31 >= a.Sk;
+            const int dq = my_qk - jb;  // slot (sb, r) sits at distance dq - (kbase_g + 8 sb + r)
+            const int vlim = CAUSAL ? dq + 1 : a.Sk - jb;  // slot keys below vlim are real keys
+            f32x4_t c0, c1;
+            const int sf = p_full >> 4, zb = p_full - 16 * sf - 4 * g;
+            const bf16x8_t qz = qmask(sf, zb);
+#define ATF16_S(i) \
+                case i: if constexpr ((i) < NSTEP) scores(kb, (i), qz, c0, c1); break;
+            switch (min(sf, NSTEP - 1)) {
+                ATF16_S(0) ATF16_S(1) ATF16_S(2) ATF16_S(3) ATF16_S(4) ATF16_S(5) ATF16_S(6) ATF16_S(7)
+                default: break;
+            }
+#undef ATF16_S
+            if (p_lo > 0) {
+                if (!diag) skipped_u += (unsigned long long)p_lo * 32u * nq;
+                else if (q_valid) skipped += (unsigned long long)p_lo * (unsigned)slots_below16(vlim, kbase_g);
+            }
+            for (int p = p_lo; p < p_full; ++p) {
+                const int s = p >> 4, gp = (p >> 2) & 3, w = p & 3;
+                u32x4 k0 = kfrag(kb, 0, s), k1 = kfrag(kb, 1, s);
+                const bool mine = g == gp;
+                k0.x = (mine && w == 0) ? k0.x : 0u; k1.x = (mine && w == 0) ? k1.x : 0u;
+                k0.y = (mine && w == 1) ? k0.y : 0u; k1.y = (mine && w == 1) ? k1.y : 0u;
+                k0.z = (mine && w == 2) ? k0.z : 0u; k1.z = (mine && w == 2) ? k1.z : 0u;
+                k0.w = (mine && w == 3) ? k0.w : 0u; k1.w = (mine && w == 3) ? k1.w : 0u;
+                bf16x8_t qs = qf[0];
+#pragma unroll
+                for (int ss = 1; ss < NSTEP; ++ss) qs = (s == ss) ? qf[ss] : qs;
+                const f32x4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qs, zero4, 0, 0, 0);
+                const f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qs, zero4, 0, 0, 0);
+                // pair p is kept at slot key c iff |dq - c| <= W_p: lim <= c (<= him)
+                const int wp = window_at(win, p);
+                const int lim = dq - wp, him = CAUSAL ? dq : dq + wp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ca = kbase_g + r, cb = kbase_g + 8 + r;
+                    c0[r] += (ca >= lim && (CAUSAL || ca <= him)) ? t0[r] : 0.f;
+                    c1[r] += (cb >= lim && (CAUSAL || cb <= him)) ? t1[r] : 0.f;
+                }
+                if (q_valid)
+                    skipped += (unsigned)(slots_below16(min(lim, vlim), kbase_g) +
+                                          (CAUSAL ? 0 : slots_below16(vlim, kbase_g) -
+                                                            slots_below16(min(vlim, him + 1), kbase_g)));
+            }
+            if (diag) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (kbase_g + r >= vlim) c0[r] = -INFINITY;
+                    if (kbase_g + 8 + r >= vlim) c1[r] = -INFINITY;
+                }
+            }
+            u32x4 pw;
+            float ls;
+            probs(c0, c1, pw, ls);
+            rescale(c0, c1, pw, ls);
+            pv(kb, pw);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+#undef ATF16_TILE_LOAD
+
+    // epilogue: lane (t, g) holds dims 16 db + 4 g + (0..3) of query t
+    const float inv = 1.f / quad_sum(l_run);
+    if (q_valid) {
+        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            u32x2 w;
+            w.x = pack_bf(o[db][0] * inv, o[db][1] * inv);
+            w.y = pack_bf(o[db][2] * inv, o[db][3] * inv);
+            *(u32x2 *)(orow + 16 * db + 4 * g) = w;
+        }
+    }
+    skipped_u += (unsigned long long)fast_cut * (NB * 32u) * nq;
+    skipped = wave_sum_u64(skipped) + skipped_u;
+    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+}
+
+// ============================================================================
 // fp32 attention (prefill and decode): plain VALU, one query per lane, keys
 // rotated on the fly per 32-key LDS tile, exact per-element window test.
 // Serves the fp32 dtype (parity workloads), not the bf16 hot path.
@@ -931,22 +1329,6 @@ __global__ __launch_bounds__(64) void attend_f32_kernel(AttnArgs a) {
 // grid (nsplit, B*Hkv*n_slabs), block 256.
 // ============================================================================
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-__device__ inline float quad_max(float x) {  // max over lanes t, t+16, t+32, t+48
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b2[0]), __uint_as_float(b2[1]));
-}
-__device__ inline float quad_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
-}
 
 // 8 bytes holding dim t of 4 consecutive keys (see the lane mapping above)
 __device__ inline u32x2 lds_read_tr16(const unsigned char *lds, unsigned byte_addr) {
@@ -1765,14 +2147,15 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
-    if (a.causal) {
-        if (d == 256) prefill_bf16_kernel<256, true><<<n_wg, prefill_waves(256) * 64, 0, s>>>(a);
-        else if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, prefill_waves(128) * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, true><<<n_wg, prefill_waves(64) * 64, 0, s>>>(a);
+    if (d == 256) {
+        if (a.causal) prefill16_bf16_kernel<256, true><<<n_wg, kPrefill16Waves * 64, 0, s>>>(a);
+        else prefill16_bf16_kernel<256, false><<<n_wg, kPrefill16Waves * 64, 0, s>>>(a);
+    } else if (a.causal) {
+        if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
     } else {
-        if (d == 256) prefill_bf16_kernel<256, false><<<n_wg, prefill_waves(256) * 64, 0, s>>>(a);
-        else if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, prefill_waves(128) * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, false><<<n_wg, prefill_waves(64) * 64, 0, s>>>(a);
+        if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
     }
     return hipGetLastError();
 }
