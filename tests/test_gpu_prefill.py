@@ -182,6 +182,29 @@ def test_bf16_workload_sizes_sampled(env, S, alpha, per_head, heads):
     check_bf16(got, ref, dense, "S=%d alpha=%g" % (S, alpha))
 
 
+@pytest.mark.parametrize("d,last_step_pair", [(128, 56), (256, 112)])
+def test_bf16_cut_reaches_last_kstep(env, d, last_step_pair):
+    """Base 1e4, alpha 0.5, S=12288: the farthest keys keep only pairs inside
+    the last MFMA K-step (16 dims at d = 128, 32 dims at d = 256), so the
+    kernels' last-step score chain and its in-step masking run; sampled rows
+    include the last query, which sees those keys."""
+    torch, oracle, atf, _ = env
+    B, Hq, Hkv, S, base, alpha = 1, 4, 2, 12288, 1e4, 0.5
+    W = atf.atf_window_table(d, base, alpha)
+    assert W[last_step_pair - 1] < S - 1 < W[last_step_pair + 3]  # cut lands inside the last step
+    log("case: last K-step d=%d S=%d" % (d, S))
+    q, k, v, out, skipped = run_prefill(env, B, Hq, Hkv, S, d, base, alpha, torch.bfloat16)
+    assert skipped == B * Hq * atf.atf_skipped_pair_products(S, d, base, alpha)
+    rows = sampled_rows(Hq, S, 6, seed=d)
+    sel = torch.as_tensor(rows, device=q.device)
+    qrows = q[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    got = out[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
+    kk, vv = k.float().cpu().numpy(), v.float().cpu().numpy()
+    ref, _ = oracle.attention(qrows, kk, vv, base=base, alpha=alpha, rows=rows, q_shape=(B, Hq, S, d))
+    dense, _ = oracle.attention(qrows, kk, vv, base=base, alpha=math.inf, rows=rows, q_shape=(B, Hq, S, d))
+    check_bf16(got, ref, dense, "last K-step d=%d" % d)
+
+
 @pytest.mark.parametrize("dtype_name", ["bfloat16", "float32"])
 def test_prepared_workspace_reused(env, dtype_name):
     """One prepare, several attend calls with different alpha: each call's
