@@ -173,6 +173,7 @@ def time_leg(torch, stream, fn, steps):
 def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     """Decode at the main decode size with GPT-J interleaved pairs (standard
     [S][d] cache); prefill at S=32K, at 128K with alpha 0.5 and 2, and at 1M;
+    a 4096-token chunk after a 126976-token prefix; non-causal prefill at 32K;
     prefill/decode with 256-dim heads."""
     out = {}
     D = DECODE
@@ -213,6 +214,59 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
         log("prefill S=%d alpha=%g: attend %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
             % (S, alpha, ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
         del q, k, v, o, ws
+
+    # chunked prefill: the last 4096 of 131072 tokens against the whole cache.
+    # The call rotates all 131072 keys, then attends the chunk; its queries are
+    # the full prefill over Sk minus the prefill over Sk - Sq, which gives the
+    # exact dropped-term count.
+    P = dict(PREFILL, S=131072)
+    Sq, Sk, d = 4096, 131072, P["d"]
+    q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], Sq, Sk, d, dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], Sk, d, atf.ATF_BF16), dtype=torch.uint8,
+                     device=dev)
+    _, got = atf.atf_prefill_chunk(q, k, v, o, rope_base=P["base"], alpha=P["alpha"], ws=ws, return_skipped=True)
+    per_head = (atf.atf_skipped_pair_products(Sk, d, P["base"], P["alpha"]) -
+                atf.atf_skipped_pair_products(Sk - Sq, d, P["base"], P["alpha"]))
+    if got != P["B"] * P["Hq"] * per_head:
+        raise SystemExit("chunked prefill dropped-term count differs from the closed form")
+    ms = time_leg(torch, stream, lambda: atf.atf_prefill_chunk(q, k, v, o, rope_base=P["base"], alpha=P["alpha"],
+                                                               ws=ws), steps)
+    n_c = Sq * (Sk - Sq) + Sq * (Sq + 1) // 2
+    flops = P["B"] * P["Hq"] * (4 * (d // 2) * n_c + 2 * d * n_c) - 4 * got
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_chunk"] = {
+        "value": P["B"] * Sq / (ms * 1e-3), "unit": "tok/s (whole call: rotate every key, attend the chunk)",
+        "ms": ms, "config": dict(P, S=None, Sq=Sq, Sk=Sk),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops}}
+    log("prefill chunk Sq=%d after %d cached: %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
+        % (Sq, Sk - Sq, ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+    del q, k, v, o, ws
+
+    # non-causal windows (|i - j| against W_p), S=32K
+    P = dict(PREFILL, S=32768)
+    S = P["S"]
+    q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], S, S, d, dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], S, d, atf.ATF_BF16), dtype=torch.uint8,
+                     device=dev)
+    atf.atf_prefill_prepare_kv(k, v, rope_base=P["base"], ws=ws)
+    got = atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=P["alpha"], causal=0, ws=ws,
+                                 return_skipped=True)
+    if got != P["B"] * P["Hq"] * atf.atf_skipped_pair_products(S, d, P["base"], P["alpha"], 0, 0):
+        raise SystemExit("non-causal prefill dropped-term count differs from the closed form")
+    ms = time_leg(torch, stream, lambda: atf.atf_prefill_attend(q, k, v, o, rope_base=P["base"], alpha=P["alpha"],
+                                                                causal=0, ws=ws), steps)
+    flops = P["B"] * P["Hq"] * (4 * (d // 2) * S * S + 2 * d * S * S) - 4 * got
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_noncausal_s%d" % S] = {
+        "value": P["B"] * S / (ms * 1e-3), "unit": "tok/s (attention kernel)", "ms": ms, "config": dict(P, causal=0),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops}}
+    log("prefill non-causal S=%d: attend %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
+        % (S, ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
+    del q, k, v, o, ws
 
     P = PREFILL_D256
     q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], P["S"], P["S"], P["d"], dtype=torch.bfloat16, device=dev)
