@@ -238,8 +238,9 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
 // lane^32 the other 16, so softmax row statistics need one lane swap), then
 // O^T += V^T P^T.  Blocks go in pairs, chain0 | chain1 + probs0 | PV0 +
 // probs1 | PV1, so the exponentials sit beside MFMA runs.  Tiles where every
-// key precedes every query of the wave and no window falls inside the tile's
-// distance range take a fast path with one pair cut for all their blocks.
+// key precedes every query of the wave (non-causal: or follows every query)
+// and no window falls inside the tile's distance range take a fast path with
+// one pair cut for all their blocks.
 //
 // Windows per 32x32 block: distances span [dmin, dmax]; pairs below
 // p_lo = p*(dmin) are dropped everywhere in the block, pairs from
@@ -660,8 +661,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
         first = false;                                                                            \
         l_run += lsum[sl];
 
-        // Fast tile (the common case, causal): for this wave every key of the
-        // tile precedes every query and no window W_p falls inside the tile's
+        // Fast tile (the common case): for this wave every key of the tile
+        // precedes every query (causal; non-causal also: follows every query,
+        // none past the end) and no window W_p falls inside the tile's
         // distance range, so all its blocks keep the same pair suffix [p_t, P)
         // with no per-element work.
         bool fast;
@@ -674,16 +676,18 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                 dmin = i0k - jl;
                 dmax = i0k + 31 - j0;
             } else {
-                // (the non-causal kernel keeps the general path: its extra
-                // masks leave no registers for a second copy of the tile body)
-                fast = false;
-                dmin = dmax = 0;
+                // every key of the tile on one side of every query of the
+                // wave, none past the end: distances |i - j| span [dmin, dmax]
+                const bool before = jl <= i0k, after = j0 > i0k + 31;
+                fast = (before || after) && jl < a.Sk;
+                dmin = before ? i0k - jl : j0 - (i0k + 31);
+                dmax = before ? i0k + 31 - j0 : jl - i0k;
             }
             const int plo_t = cut_below(win, dmin);
             p_t = cut_below(win, dmax);
             fast = fast && plo_t == p_t;
         }
-        if (CAUSAL && fast) {
+        if (fast) {
             fast_cut += (unsigned)p_t;
             const int sf = p_t >> 3, zb = p_t - 8 * sf - koff0;
 #pragma unroll
