@@ -2110,21 +2110,40 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// grid B*Hq, block D.
+// grid B*Hq, block D.  Splits are read CU at a time (indices clamped to the
+// row's last split, extra values masked), so CU loads are in flight per step;
+// the sum still runs in split order.
 template <int D, bool PAGED>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int CU = 8;
     const int row = blockIdx.x, c = threadIdx.x;
     const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
     const int ns = PAGED ? paged_nsplit(a, row / a.Hq) : a.nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (D + 2) + D]);
+    for (int s0 = 0; s0 < ns; s0 += CU) {
+        float m[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) m[u] = pr[min(s0 + u, ns - 1) * (D + 2) + D];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) M = fmaxf(M, m[u]);  // a repeated last split changes no max
+    }
     float num = 0.f, den = 0.f;
-    for (int s = 0; s < ns; ++s) {
-        const float ms = pr[s * (D + 2) + D];
-        if (ms == -INFINITY) continue;
-        const float f = fast_exp2(ms - M);
-        num += f * pr[s * (D + 2) + c];
-        den += f * pr[s * (D + 2) + D + 1];
+    for (int s0 = 0; s0 < ns; s0 += CU) {
+        float m[CU], o[CU], l[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+            const float *ps = pr + min(s0 + u, ns - 1) * (D + 2);
+            m[u] = ps[D];
+            o[u] = ps[c];
+            l[u] = ps[D + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+            if (s0 + u >= ns || m[u] == -INFINITY) continue;
+            const float f = fast_exp2(m[u] - M);
+            num += f * o[u];
+            den += f * l[u];
+        }
     }
     const float r = num / den;
     ((__bf16 *)a.out)[(long long)row * D + c] = (__bf16)r;
