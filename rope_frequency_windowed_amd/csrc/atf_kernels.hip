@@ -1673,13 +1673,34 @@ __device__ inline long long paged_total_len(const DecodeArgs &a) {
     for (int i = lane; i < a.B; i += 64) tot += (unsigned long long)min(max(a.seq_lens[i], 1), a.S);
     return (long long)wave_sum_u64(tot);
 }
-__device__ inline int paged_nsplit_of(const DecodeArgs &a, int b, long long tot) {
+// Splits of sequence b: its share of `bud` splits, rounded up (so no split
+// holds more than the batch's average share of keys), at least one.
+__device__ inline int paged_nsplit_of(const DecodeArgs &a, int b, long long tot, long long bud) {
     const long long L = min(max(a.seq_lens[b], 1), a.S);
-    const long long want = (L * a.split_budget + tot - 1) / tot;
+    const long long want = (L * bud + tot - 1) / tot;
     const long long nch = (L + kKeyTile - 1) / kKeyTile;
     return (int)max(1ll, min(want, min((long long)a.nsplit, nch)));
 }
-__device__ inline int paged_nsplit(const DecodeArgs &a, int b) { return paged_nsplit_of(a, b, paged_total_len(a)); }
+// The shares are taken of a budget lowered by the rounding excess until the
+// batch's splits fit the workgroups resident at once (split_budget): one
+// split more than that would run as a second wave and double the time.
+// Every lane of the wave must call it (one sequence per lane, then a wave sum).
+__device__ inline long long paged_budget(const DecodeArgs &a, long long tot) {
+    const int lane = threadIdx.x & 63;
+    long long bud = a.split_budget;
+    for (int it = 0; it < 8; ++it) {
+        unsigned long long part = 0;
+        for (int i = lane; i < a.B; i += 64) part += (unsigned long long)paged_nsplit_of(a, i, tot, bud);
+        const long long total = (long long)wave_sum_u64(part);
+        if (total <= a.split_budget || bud <= 1) break;
+        bud = max(1ll, bud - (total - a.split_budget));
+    }
+    return bud;
+}
+__device__ inline int paged_nsplit(const DecodeArgs &a, int b) {
+    const long long tot = paged_total_len(a);
+    return paged_nsplit_of(a, b, tot, paged_budget(a, tot));
+}
 
 // Algorithmic bytes of keys [0, j) of a sequence of S keys (decode query after
 // them): 2d per value row plus 4 per kept pair, where pair p (finite W_p) is
@@ -1810,9 +1831,10 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     if (PAGED) {
         hk = blockIdx.y / a.n_slabs;
         const long long tot = paged_total_len(a);
+        const long long bud = paged_budget(a, tot);
         b = -1;
         for (int i = 0, c0 = 0; i < a.B; ++i) {
-            const int n = paged_nsplit_of(a, i, tot);
+            const int n = paged_nsplit_of(a, i, tot, bud);
             if (split < c0 + n) { b = i; split -= c0; nsb = n; break; }
             c0 += n;
         }
