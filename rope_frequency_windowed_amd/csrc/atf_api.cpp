@@ -107,8 +107,10 @@ int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
     const int64_t units = (int64_t)B * Hkv * n_slabs;
     const int64_t nchunks = (S + kKeyTile - 1) / kKeyTile;
     // aim for one round of resident workgroups; byte-balanced splits then
-    // finish together.  At least one chunk per split.
-    int64_t ns = (decode_resident(d) + units - 1) / units;
+    // finish together.  Rounded down: one workgroup over the resident count
+    // would run as a second round and double the time.  At least one chunk
+    // per split.
+    int64_t ns = decode_resident(d) / units;
     ns = std::min<int64_t>(ns, kMaxSplits);
     ns = std::min<int64_t>(ns, nchunks);
     return (int)std::max<int64_t>(ns, 1);
@@ -127,7 +129,7 @@ void paged_plan(int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, int &budget
     const int n_slabs = (group + kDecodeHeads - 1) / kDecodeHeads;
     const int64_t units = (int64_t)Hkv * n_slabs;
     const int64_t nchunks = (max_len + kKeyTile - 1) / kKeyTile;
-    const int64_t b = std::max<int64_t>(1, (decode_resident(d) + units - 1) / units);
+    const int64_t b = std::max<int64_t>(1, decode_resident(d) / units);  // rounded down, as above
     budget = (int)b;
     nsplit_max = (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(b, kMaxSplits), nchunks));
 }
