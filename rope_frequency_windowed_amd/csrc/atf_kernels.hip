@@ -1832,11 +1832,29 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         hk = blockIdx.y / a.n_slabs;
         const long long tot = paged_total_len(a);
         const long long bud = paged_budget(a, tot);
+        // the sequence owning split id `split`: 64 sequences per step, one per
+        // lane, with a wave prefix sum of their split counts
         b = -1;
-        for (int i = 0, c0 = 0; i < a.B; ++i) {
-            const int n = paged_nsplit_of(a, i, tot, bud);
-            if (split < c0 + n) { b = i; split -= c0; nsb = n; break; }
-            c0 += n;
+        const int lane_ = threadIdx.x & 63;
+        for (int base_i = 0, c0 = 0; base_i < a.B; base_i += 64) {
+            const int i = base_i + lane_;
+            const int n = i < a.B ? paged_nsplit_of(a, i, tot, bud) : 0;
+            int incl = n;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off, 64);
+                if (lane_ >= off) incl += y;
+            }
+            const int chunk = __shfl(incl, 63, 64);
+            if (split < c0 + chunk) {
+                const int first = __builtin_ctzll(__ballot(split < c0 + incl));
+                const int excl = __shfl(incl - n, first, 64);
+                nsb = __shfl(n, first, 64);
+                b = base_i + first;
+                split -= c0 + excl;
+                break;
+            }
+            c0 += chunk;
         }
         if (b < 0) return;  // past the batch's splits (uniform)
     } else {

@@ -79,6 +79,22 @@ def test_paged_bf16(env, B, Hq, Hkv, lens, d, base, alpha):
     assert skipped == ref_skipped == Hq * sum(atf.atf_skipped_pair_products(S, d, base, alpha, 1, 1) for S in lens)
 
 
+def test_paged_large_batch(env):
+    """150 sequences of seeded random lengths 1..1200: the split ids are mapped
+    to sequences 64 at a time, so three scan steps and a sequence straddling
+    the first step boundary are exercised; every row against the oracle."""
+    torch, oracle, atf, _ = env
+    lens = [int(x) for x in np.random.default_rng(150).integers(1, 1201, size=150)]
+    B, Hq, Hkv, d, base, alpha = len(lens), 2, 1, 128, 1e6, 1.0
+    log("case: paged decode, %d sequences" % B)
+    q, k, v, kpool, vpool, pt, sl, max_len = build_paged(env, B, Hq, Hkv, lens, d, base)
+    out, skipped = atf.atf_decode_paged(q, kpool, vpool, pt, sl, max_len=max_len, rope_base=base, alpha=alpha,
+                                        return_skipped=True)
+    torch.cuda.synchronize()
+    ref_skipped = check_against_oracle(env, q, k, v, out, lens, base, alpha, label="paged large batch")
+    assert skipped == ref_skipped == Hq * sum(atf.atf_skipped_pair_products(S, d, base, alpha, 1, 1) for S in lens)
+
+
 def test_paged_max_len_above_lengths(env):
     """max_len (planning bound) larger than every length: same answer."""
     torch, oracle, atf, _ = env
