@@ -159,11 +159,27 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
  * atf_prefill (Sq == Sk is atf_prefill).  Source page "ATFlash: ..."
  * (sudo-ai.de), section "Die Zahlen - und ihre Grenze": the method drops into
  * the prefill path unchanged, and a prefill continued over a cached prefix is
- * that path with a query offset.  Needs 1 <= Sq <= Sk and
+ * that path with a query offset.  Needs 1 <= Sq <= Sk and at least
  * atf_prefill_workspace_bytes(B, Hkv, Sk, d, dtype) bytes of workspace (the
- * rotated keys of all Sk tokens).  Errors: Sq < 1 or Sq > Sk is
- * ATF_ERR_INVALID_ARG; otherwise as atf_prefill with S = Sk.
+ * rotated keys of all Sk tokens).  Given atf_prefill_chunk_workspace_bytes
+ * bytes or more, the bf16 path splits each query tile's key range over
+ * several workgroups when the chunk is too short to fill the GPU, and merges
+ * the splits' partial results (unnormalised output, reference maximum, sum)
+ * in a combine kernel; the result is the same softmax up to fp32 rounding
+ * order.  Errors: Sq < 1 or Sq > Sk is ATF_ERR_INVALID_ARG; otherwise as
+ * atf_prefill with S = Sk.
  */
+/*
+ * Workspace bytes with which atf_prefill_chunk may split the key range: the
+ * prepared keys and values of atf_prefill_workspace_bytes(B, Hkv, Sk, d,
+ * dtype), followed by B*Hq*Sq*n_split rows of d + 2 floats of partials when
+ * the planner splits (n_split <= 64).  Equal to atf_prefill_workspace_bytes
+ * when no split would help (fp32, or a chunk that already fills the GPU).
+ * Returns 0 for shapes atf_prefill_chunk rejects.
+ */
+size_t atf_prefill_chunk_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d,
+                                         atf_dtype dtype);
+
 atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *out,
                              int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d,
                              int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,

@@ -25,7 +25,8 @@ W_INF = np.iinfo(np.int64).max
 EXPORTED = (
     "atf_status_string", "atf_version", "atf_window_table", "atf_skipped_pair_products",
     "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
-    "atf_prefill_attend", "atf_prefill_chunk", "atf_decode_workspace_bytes", "atf_decode",
+    "atf_prefill_attend", "atf_prefill_chunk", "atf_prefill_chunk_workspace_bytes",
+    "atf_decode_workspace_bytes", "atf_decode",
     "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
     "atf_paged_page_bytes", "atf_decode_paged_workspace_bytes", "atf_paged_write", "atf_decode_paged",
 )
@@ -61,6 +62,8 @@ def _lib():
     lib.atf_skipped_pair_products.restype = ctypes.c_int
     lib.atf_prefill_workspace_bytes.argtypes = [i32, i32, i64, i32, ctypes.c_int]
     lib.atf_prefill_workspace_bytes.restype = sz
+    lib.atf_prefill_chunk_workspace_bytes.argtypes = [i32, i32, i32, i64, i64, i32, ctypes.c_int]
+    lib.atf_prefill_chunk_workspace_bytes.restype = sz
     lib.atf_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f64, f64, i32, i64,
                                 ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill.restype = ctypes.c_int
@@ -133,6 +136,10 @@ def atf_skipped_pair_products(S: int, d: int, rope_base: float, alpha: float, ca
 
 def atf_prefill_workspace_bytes(B: int, Hkv: int, S: int, d: int, dtype: int) -> int:
     return int(_lib().atf_prefill_workspace_bytes(B, Hkv, S, d, dtype))
+
+
+def atf_prefill_chunk_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, dtype: int) -> int:
+    return int(_lib().atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, dtype))
 
 
 def atf_decode_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:
@@ -249,7 +256,7 @@ def atf_prefill_chunk(q, k, v, out=None, *, rope_base: float, alpha: float, caus
     code = _dtype_code(q)
     if out is None:
         out = _torch().empty_like(q)
-    nbytes = atf_prefill_workspace_bytes(B, Hkv, Sk, d, code)
+    nbytes = atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, code)
     if ws is None:
         ws = workspace(nbytes, q.device, "prefill")
     skipped = ctypes.c_uint64(0)

@@ -89,6 +89,28 @@ size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype 
     return kHeaderBytes + 2 * per;  // rotated keys + transposed values
 }
 
+// Key-range splits of a chunked prefill (bf16).  A small chunk has few query
+// tiles, so few workgroups walk the whole cache; splitting each tile's key
+// range brings the grid to about two rounds of resident workgroups (the
+// prefill kernels run one workgroup per CU), keeping at least two key tiles
+// per split.  The splits' partials are merged by a combine kernel.
+constexpr int kMaxKSplit = 64;
+int chunk_ksplit(int32_t B, int32_t Hq, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
+    if (dtype != ATF_BF16) return 1;
+    const int64_t qt = prefill_query_tile(d);
+    const int64_t active = (Sq + qt - 1) / qt * B * Hq;  // workgroups with work
+    const int64_t kt = d == 256 ? kPrefill16Keys : kPrefillKeys;
+    const int64_t max_by_keys = std::max<int64_t>(1, Sk / kt / 2);
+    const int64_t want = 512 / active;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, max_by_keys), kMaxKSplit));
+}
+
+size_t chunk_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
+    const int ns = chunk_ksplit(B, Hq, Sq, Sk, d, dtype);
+    const size_t part = ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0;
+    return prefill_ws_bytes(B, Hkv, Sk, d, dtype) + part;
+}
+
 // ---------------------------------------------------------------- decode plan
 
 struct DecodePlan {
@@ -201,7 +223,7 @@ atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) 
 atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
                        int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, int32_t layout, double rope_base, double alpha,
                        int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
-                       uint64_t *skipped_out, hipStream_t s) {
+                       uint64_t *skipped_out, hipStream_t s, int n_ksplit = 1) {
     if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
     if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
     if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
@@ -241,6 +263,9 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
         a.vt = ws + per;
         a.n_qtiles = (int)((Sq + prefill_query_tile(d) - 1) / prefill_query_tile(d));
         a.n_groups = a.n_qtiles * B * Hkv;
+        a.n_ksplit = n_ksplit;
+        // partials of a key-range split follow the prepared keys and values
+        a.part = n_ksplit > 1 ? (float *)((char *)workspace + prefill_ws_bytes(B, Hkv, Sk, d, dtype)) : nullptr;
         e = launch_prefill_bf16(a, d, s);
     }
     if (e != hipSuccess) return ATF_ERR_HIP;
@@ -373,9 +398,18 @@ atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *
     st = atf_prefill_prepare_kv(k, v, B, Hkv, Sk, d, rope_layout, rope_base, pos0, dtype, workspace,
                                 workspace_bytes, stream);
     if (st != ATF_OK) return st;
+    // split the key range when the workspace has room for the partials
+    const int ns = workspace_bytes >= chunk_ws_bytes(B, Hq, Hkv, Sq, Sk, d, dtype)
+                       ? chunk_ksplit(B, Hq, Sq, Sk, d, dtype) : 1;
     return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_layout, rope_base, alpha, causal, pos0, dtype,
-                       workspace,
-                       workspace_bytes, skipped_out, (hipStream_t)stream);
+                       workspace, workspace_bytes, skipped_out, (hipStream_t)stream, ns);
+}
+
+size_t atf_prefill_chunk_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d,
+                                         atf_dtype dtype) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sq > Sk || (!supported_d(d))) return 0;
+    if (dtype != ATF_F32 && dtype != ATF_BF16) return 0;
+    return chunk_ws_bytes(B, Hq, Hkv, Sq, Sk, d, dtype);
 }
 
 size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {

@@ -533,6 +533,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     // windows applying to |i - j|
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
+    // key tiles of this workgroup's split of the key range: [kt0, kt1)
+    const int sp = blockIdx.y;
+    const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
     // wave's n-th 1 KB piece lands at LDS byte piece*1024 + 16 l (lane-linear),
@@ -614,13 +617,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned vbase_lane = KT_BYTES + (unsigned)qi * 128;
     const unsigned vz = (unsigned)((swz8(qi) ^ half) << 4);
 
-    ATF_TILE_LOAD(0, 0);
+    if (kt0 < kt1) ATF_TILE_LOAD(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < n_kt) ATF_TILE_LOAD(kt + 1, buf ^ 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        if (kt + 1 < kt1) ATF_TILE_LOAD(kt + 1, buf ^ 1);
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * KT;
 
@@ -641,7 +644,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             float bm = sacc[sl][0];                                                               \
             _Pragma("unroll") for (int r = 1; r < 16; ++r) bm = fmaxf(bm, sacc[sl][r]);           \
             bm = partner_max(bm);                                                                 \
-            const float m_new = first ? bf16_ceil(m_ref + bm) : fmaxf(m_ref, bf16_ceil(m_ref + bm)); \
+            /* (first block: a query with all its keys masked keeps the reference) */              \
+            const float m_new = first ? (bm == -INFINITY ? m_ref : bf16_ceil(m_ref + bm))          \
+                                      : fmaxf(m_ref, bf16_ceil(m_ref + bm));                       \
             const float shift = m_new - m_ref;                                                    \
             if (!first) {                                                                         \
                 const float corr = fast_exp2(-shift);                                             \
@@ -811,9 +816,28 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     }
 #undef ATF_TILE_LOAD
 
-    // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3)
-    const float inv = 1.f / partner_sum(l_run);
-    if (q_valid) {
+    // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3).
+    // A key-range split instead writes its unnormalised O, m_ref and l (m =
+    // -inf when the split holds none of the query's mass) for the combine.
+    const float l_tot = partner_sum(l_run);
+    if (a.n_ksplit > 1) {
+        if (q_valid) {
+            float *pr = a.part + ((((long long)(b * a.Hq + h) * a.Sq + my_q) * a.n_ksplit) + sp) * (D + 2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {  // rows of d + 2 floats are 8-byte aligned
+                    float *pd = pr + 32 * db + 8 * g4 + 4 * half;
+                    *(float2 *)pd = make_float2(o[db][4 * g4], o[db][4 * g4 + 1]);
+                    *(float2 *)(pd + 2) = make_float2(o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
+                }
+            if (half == 0) {
+                pr[D] = l_tot > 0.f ? m_ref : -INFINITY;
+                pr[D + 1] = l_tot;
+            }
+        }
+    } else if (q_valid) {
+        const float inv = 1.f / l_tot;
         unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -936,6 +960,9 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
+    // key tiles of this workgroup's split of the key range: [kt0, kt1)
+    const int sp = blockIdx.y;
+    const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
 
     // Tile loader: piece m (1 KB) of K' lands lane-linear at LDS byte 1024 m +
     // 16 l, i.e. row (1024 m + 16 l) / row_bytes, physical chunk l % CH; the
@@ -992,13 +1019,13 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const unsigned ksw0 = (unsigned)kswz_sub(krow_t), ksw1 = (unsigned)kswz_sub(krow_t + 8);
     const unsigned vrow_base = KT_BYTES + (unsigned)t * 128;
 
-    ATF16_TILE_LOAD(0, 0);
+    if (kt0 < kt1) ATF16_TILE_LOAD(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < n_kt) ATF16_TILE_LOAD(kt + 1, buf ^ 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        if (kt + 1 < kt1) ATF16_TILE_LOAD(kt + 1, buf ^ 1);
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * KT;
 
@@ -1049,7 +1076,8 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
                 float bm = fmaxf(fmaxf(fmaxf(c0[0], c0[1]), fmaxf(c0[2], c0[3])),
                                  fmaxf(fmaxf(c1[0], c1[1]), fmaxf(c1[2], c1[3])));
                 bm = quad_max(bm);  // block max relative to m_ref
-                const float m_new = first ? m_ref + bm : fmaxf(m_ref, m_ref + bm);
+                // (first block: a query with all its keys masked keeps the reference)
+                const float m_new = first ? (bm == -INFINITY ? m_ref : m_ref + bm) : fmaxf(m_ref, m_ref + bm);
                 const float shift = m_new - m_ref;
                 if (!first) {
                     const float corr = fast_exp2(-shift);
@@ -1192,9 +1220,24 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     }
 #undef ATF16_TILE_LOAD
 
-    // epilogue: lane (t, g) holds dims 16 db + 4 g + (0..3) of query t
-    const float inv = 1.f / quad_sum(l_run);
-    if (q_valid) {
+    // epilogue: lane (t, g) holds dims 16 db + 4 g + (0..3) of query t; a
+    // key-range split writes its unnormalised O, m_ref and l for the combine
+    const float l_tot = quad_sum(l_run);
+    if (a.n_ksplit > 1) {
+        if (q_valid) {
+            float *pr = a.part + ((((long long)(b * a.Hq + h) * a.Sq + my_q) * a.n_ksplit) + sp) * (D + 2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {  // rows of d + 2 floats are 8-byte aligned
+                *(float2 *)(pr + 16 * db + 4 * g) = make_float2(o[db][0], o[db][1]);
+                *(float2 *)(pr + 16 * db + 4 * g + 2) = make_float2(o[db][2], o[db][3]);
+            }
+            if (g == 0) {
+                pr[D] = l_tot > 0.f ? m_ref : -INFINITY;
+                pr[D + 1] = l_tot;
+            }
+        }
+    } else if (q_valid) {
+        const float inv = 1.f / l_tot;
         unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -2149,16 +2192,13 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 }
 
 
-// Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// grid B*Hq, block D.  Splits are read CU at a time (indices clamped to the
-// row's last split, extra values masked), so CU loads are in flight per step;
-// the sum still runs in split order.
-template <int D, bool PAGED>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+// Merge the ns split partials of one row (pr[s * (D + 2) + ...] = o..., m, l):
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, for dim c.  Splits are
+// read CU at a time (indices clamped to the row's last split, extra values
+// masked), so CU loads are in flight per step; the sum runs in split order.
+template <int D>
+__device__ inline float combine_row(const float *pr, int ns, int c) {
     constexpr int CU = 8;
-    const int row = blockIdx.x, c = threadIdx.x;
-    const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
-    const int ns = PAGED ? paged_nsplit(a, row / a.Hq) : a.nsplit;
     float M = -INFINITY;
     for (int s0 = 0; s0 < ns; s0 += CU) {
         float m[CU];
@@ -2185,8 +2225,25 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
             den += f * l[u];
         }
     }
-    const float r = num / den;
-    ((__bf16 *)a.out)[(long long)row * D + c] = (__bf16)r;
+    return num / den;
+}
+
+// Decode: grid B*Hq, block D.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    const int row = blockIdx.x, c = threadIdx.x;
+    const float *pr = a.part + (long long)row * a.nsplit * (D + 2);
+    const int ns = PAGED ? paged_nsplit(a, row / a.Hq) : a.nsplit;
+    ((__bf16 *)a.out)[(long long)row * D + c] = (__bf16)combine_row<D>(pr, ns, c);
+}
+
+// Prefill split over the key range: grid B*Hq*Sq (one query row each), block D.
+template <int D>
+__global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
+    const long long row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float *pr = a.part + row * a.n_ksplit * (D + 2);
+    ((__bf16 *)a.out)[row * D + c] = (__bf16)combine_row<D>(pr, a.n_ksplit, c);
 }
 
 __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
@@ -2209,17 +2266,24 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
-    const unsigned n_wg = (unsigned)(((a.n_groups + 7) / 8) * 8 * a.group);
+    // x: (query tile, kv head, XCD slot) work items; y: split of the key range
+    const dim3 grid((unsigned)(((a.n_groups + 7) / 8) * 8 * a.group), (unsigned)a.n_ksplit);
     if (d == 256) {
-        if (a.causal) prefill16_bf16_kernel<256, true><<<n_wg, kPrefill16Waves * 64, 0, s>>>(a);
-        else prefill16_bf16_kernel<256, false><<<n_wg, kPrefill16Waves * 64, 0, s>>>(a);
+        if (a.causal) prefill16_bf16_kernel<256, true><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
+        else prefill16_bf16_kernel<256, false><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
     } else if (a.causal) {
-        if (d == 128) prefill_bf16_kernel<128, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, true><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        if (d == 128) prefill_bf16_kernel<128, true><<<grid, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, true><<<grid, kPrefillWaves * 64, 0, s>>>(a);
     } else {
-        if (d == 128) prefill_bf16_kernel<128, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
-        else prefill_bf16_kernel<64, false><<<n_wg, kPrefillWaves * 64, 0, s>>>(a);
+        if (d == 128) prefill_bf16_kernel<128, false><<<grid, kPrefillWaves * 64, 0, s>>>(a);
+        else prefill_bf16_kernel<64, false><<<grid, kPrefillWaves * 64, 0, s>>>(a);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.n_ksplit <= 1) return e;
+    const unsigned rows = (unsigned)((long long)a.B * a.Hq * a.Sq);
+    if (d == 256) prefill_combine_kernel<256><<<rows, 256, 0, s>>>(a);
+    else if (d == 128) prefill_combine_kernel<128><<<rows, 128, 0, s>>>(a);
+    else prefill_combine_kernel<64><<<rows, 64, 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -149,6 +149,28 @@ def test_workspace_sizes(lib):
     assert atf.atf_decode_workspace_bytes(1, 3, 2, 10, 128) == 0
 
 
+def test_chunk_workspace_sizes(lib):
+    pre = atf.atf_prefill_workspace_bytes(1, 4, 32768, 128, atf.ATF_BF16)
+    # 16 queries, 4 heads: one query tile per head, 512 // 4 = 128 capped at 64 splits
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 32768, 128, atf.ATF_BF16) == \
+        pre + 4 * 16 * 64 * 130 * 4
+    # at most Sk / 256 splits (two 128-key tiles each)
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 1000, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 4 * 16 * 3 * 130 * 4
+    # a chunk that fills the GPU by itself, fp32, or a too-short key range: no partials
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 32768, 32768, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 32768, 128, atf.ATF_BF16)
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 32768, 128, atf.ATF_F32) == 256
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 200, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 200, 128, atf.ATF_BF16)
+    # d = 256: 64-key tiles, 128-query tiles
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 2, 1, 100, 1500, 256, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + 2 * 100 * 11 * 258 * 4
+    for bad in ((1, 3, 2, 16, 100, 128), (1, 4, 4, 0, 100, 128), (1, 4, 4, 101, 100, 128),
+                (1, 4, 4, 16, 100, 96)):
+        assert atf.atf_prefill_chunk_workspace_bytes(*bad, atf.ATF_BF16) == 0
+
+
 def test_status_strings(lib):
     for code in range(5):
         assert lib.atf_status_string(code).decode().startswith("ATF_")

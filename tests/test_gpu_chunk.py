@@ -92,13 +92,18 @@ def test_chunk_position_shift(env, pos0):
 
 
 def test_chunk_without_prefix_is_prefill(env):
-    """Sq == Sk: atf_prefill_chunk and atf_prefill agree bit for bit."""
+    """Sq == Sk: given the minimum workspace (no key split), atf_prefill_chunk
+    and atf_prefill agree bit for bit; with the split they agree to rounding."""
     torch, oracle, atf, inputs = env
-    q, k, v = inputs.make_qkv(1, 4, 2, 700, 700, 128, dtype=torch.bfloat16, device=torch.device("cuda:0"))
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_qkv(1, 4, 2, 700, 700, 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(1, 2, 700, 128, atf.ATF_BF16), dtype=torch.uint8, device=dev)
     a = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=1.0)
-    b = atf.atf_prefill_chunk(q, k, v, rope_base=1e6, alpha=1.0)
+    b = atf.atf_prefill_chunk(q, k, v, rope_base=1e6, alpha=1.0, ws=ws)
+    c = atf.atf_prefill_chunk(q, k, v, rope_base=1e6, alpha=1.0)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    check_bf16(c.float().cpu().numpy(), a.float().cpu().numpy(), None, "split chunk vs prefill")
 
 
 def test_chunk_matches_tail_of_full_prefill(env):
@@ -144,3 +149,44 @@ def test_chunk_long_prefix_sampled(env):
     dense, _ = oracle.attention(qrows, kk, vv, base=base, alpha=math.inf, q_pos0=Sk - Sq, k_pos0=0,
                                 rows=rows, q_shape=(B, Hq, Sq, d))
     check_bf16(got, ref, dense, "chunk long prefix")
+
+
+@pytest.mark.parametrize("d,causal", [(64, 1), (128, 1), (128, 0), (256, 1), (256, 0)])
+def test_chunk_key_split_matches_unsplit(env, d, causal):
+    """A short chunk over a long prefix: with the larger workspace the key
+    range of each query tile is split over workgroups and merged by the
+    combine kernel; with the minimum workspace it is not.  Both against the
+    oracle, with the same dropped-term count."""
+    torch, oracle, atf, inputs = env
+    B, Hq, Hkv, Sq, Sk, base, alpha = 1, 4, 2, 40, 3000, 1e6, 1.0
+    log("case: chunk key split d=%d causal=%d" % (d, causal))
+    dev = torch.device("cuda:0")
+    small = atf.atf_prefill_workspace_bytes(B, Hkv, Sk, d, atf.ATF_BF16)
+    big = atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16)
+    assert big > small  # the planner splits this shape
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, Sq, Sk, d, dtype=torch.bfloat16, device=dev)
+    outs = []
+    for nb in (small, big):
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        outs.append(atf.atf_prefill_chunk(q, k, v, rope_base=base, alpha=alpha, causal=causal, ws=ws,
+                                          return_skipped=True))
+    torch.cuda.synchronize()
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, causal=bool(causal), q_pos0=Sk - Sq,
+                                        k_pos0=0)
+    for (out, skipped), name in zip(outs, ("unsplit", "split")):
+        check_bf16(out.float().cpu().numpy(), ref, None, "chunk %s d=%d causal=%d" % (name, d, causal))
+        assert skipped == ref_skipped
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_chunk_short_after_long_prefix(env, d):
+    """16 queries after 32752 cached tokens: the planner's widest splits
+    (64 per query tile), every row against the oracle."""
+    torch, oracle, atf, _ = env
+    B, Hq, Hkv, Sq, Sk, base, alpha = 1, 4, 1, 16, 32768, 1e6, 1.0
+    log("case: chunk Sq=%d Sk=%d d=%d" % (Sq, Sk, d))
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
+    dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, dense, "chunk short after long prefix d=%d" % d)
+    assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
