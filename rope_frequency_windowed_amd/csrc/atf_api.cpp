@@ -89,16 +89,32 @@ size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype 
     return kHeaderBytes + 2 * per;  // rotated keys + transposed values
 }
 
+// bf16 prefill work items.  Unpacked: a query tile of prefill_query_tile(d)
+// rows of one head (a wave per 32 rows, 16 at d = 256).  Head packed: one
+// wave's rows of up to 8 heads sharing a kv head, so a short chunk does not
+// run mostly empty tiles (a 16-query chunk fills 1/16 of a 256-row tile).
+// Packed when it runs fewer wave rows (its idle waves included).
+struct PrefillPlan {
+    int hpack, n_qtiles, group;  // group: heads per kv head, or (packed) slabs of 8 heads
+};
+PrefillPlan prefill_plan(int32_t Hq, int32_t Hkv, int64_t Sq, int32_t d) {
+    const int64_t qt = prefill_query_tile(d), rows = d == 256 ? 16 : 32, nw = qt / rows;
+    const int group = Hq / Hkv, slabs = (int)((group + nw - 1) / nw);
+    const int64_t n_tiles = (Sq + qt - 1) / qt, n_blocks = (Sq + rows - 1) / rows;
+    if (n_blocks * rows * slabs * nw * Hkv < n_tiles * qt * Hq) return {1, (int)n_blocks, slabs};
+    return {0, (int)n_tiles, group};
+}
+
 // Key-range splits of a chunked prefill (bf16).  A small chunk has few query
 // tiles, so few workgroups walk the whole cache; splitting each tile's key
 // range brings the grid to about two rounds of resident workgroups (the
 // prefill kernels run one workgroup per CU), keeping at least two key tiles
 // per split.  The splits' partials are merged by a combine kernel.
 constexpr int kMaxKSplit = 64;
-int chunk_ksplit(int32_t B, int32_t Hq, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
+int chunk_ksplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
     if (dtype != ATF_BF16) return 1;
-    const int64_t qt = prefill_query_tile(d);
-    const int64_t active = (Sq + qt - 1) / qt * B * Hq;  // workgroups with work
+    const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
+    const int64_t active = (int64_t)pl.n_qtiles * B * Hkv * pl.group;  // workgroups with work
     const int64_t kt = d == 256 ? kPrefill16Keys : kPrefillKeys;
     const int64_t max_by_keys = std::max<int64_t>(1, Sk / kt / 2);
     const int64_t want = 512 / active;
@@ -106,7 +122,7 @@ int chunk_ksplit(int32_t B, int32_t Hq, int64_t Sq, int64_t Sk, int32_t d, atf_d
 }
 
 size_t chunk_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
-    const int ns = chunk_ksplit(B, Hq, Sq, Sk, d, dtype);
+    const int ns = chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, dtype);
     const size_t part = ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0;
     return prefill_ws_bytes(B, Hkv, Sk, d, dtype) + part;
 }
@@ -261,7 +277,10 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
         const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
         a.krot = ws;
         a.vt = ws + per;
-        a.n_qtiles = (int)((Sq + prefill_query_tile(d) - 1) / prefill_query_tile(d));
+        const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
+        a.hpack = pl.hpack;
+        a.n_qtiles = pl.n_qtiles;
+        a.group = pl.group;
         a.n_groups = a.n_qtiles * B * Hkv;
         a.n_ksplit = n_ksplit;
         // partials of a key-range split follow the prepared keys and values
@@ -400,7 +419,7 @@ atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *
     if (st != ATF_OK) return st;
     // split the key range when the workspace has room for the partials
     const int ns = workspace_bytes >= chunk_ws_bytes(B, Hq, Hkv, Sq, Sk, d, dtype)
-                       ? chunk_ksplit(B, Hq, Sq, Sk, d, dtype) : 1;
+                       ? chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, dtype) : 1;
     return attend_impl(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, rope_layout, rope_base, alpha, causal, pos0, dtype,
                        workspace, workspace_bytes, skipped_out, (hipStream_t)stream, ns);
 }

@@ -62,6 +62,7 @@ struct AttnArgs {
     int gptj;                         // rotary pairs: 0 = dims (p, p + d/2), 1 = dims (2p, 2p + 1)
     int n_qtiles, n_groups;           // work decomposition
     int n_ksplit;                     // key-range splits (grid.y); > 1: partials to `part`, then a combine
+    int hpack;                        // 1: a work item is one query block of up to 8 heads sharing a kv head
     float *part;                      // [B*Hq*Sq][n_ksplit][d + 2]  (o..., m, l), n_ksplit > 1 only
     float scale_log2;                 // log2(e) / sqrt(d)
     int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)

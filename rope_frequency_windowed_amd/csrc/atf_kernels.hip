@@ -475,6 +475,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
 
     // ---- work item: longest query tiles first; the group heads sharing one kv
     // head run on one XCD (workgroup ids are dealt to the 8 XCDs round robin).
+    // A work item is QT query rows of one head (wave w: rows 32 w ..), or, head
+    // packed (a.hpack, for short chunks), 32 query rows of up to NW heads that
+    // share the kv head (wave w: head NW * slab + w of the group, the same
+    // rows), so one LDS key tile serves NW heads; a.group then counts slabs.
     const int L = blockIdx.x;
     const int xcd = L & 7, slot = L >> 3;
     const int gi = (slot / a.group) * 8 + xcd;
@@ -484,18 +488,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const int qt = a.n_qtiles - 1 - gi / per_qt;
     const int rem = gi % per_qt;
     const int b = rem / a.Hkv, hk = rem % a.Hkv;
-    const int h = hk * a.group + g;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int qi = lane & 31, half = lane >> 5;
-    const int i0 = qt * QT + wave * 32;  // first query row of this wave
+    const int hgroup = a.Hq / a.Hkv;
+    const int hw = a.hpack ? NW * g + wave : 0;  // packed: head within the kv group
+    const int h = a.hpack ? hk * hgroup + min(hw, hgroup - 1) : hk * a.group + g;
+    const int QS = a.hpack ? 32 : QT;            // query rows of the work item
+    const int i0 = a.hpack ? qt * 32 : qt * QT + wave * 32;  // first query row of this wave
     const int my_q = i0 + qi;
-    const bool q_valid = my_q < a.Sq;
+    const bool q_valid = my_q < a.Sq && hw < hgroup;
     // Causal tests and distances run in key-index units: query row i sits at
     // key index i + qoff (qoff = Sk - Sq > 0 when a prefix of cached keys
     // precedes the query chunk).
     const int qoff = (int)(a.q_pos0 - a.k_pos0);
-    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QT + qoff;
+    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QS + qoff;
     const WaveWin<P> win = load_windows<P>(a.W);
 
     // ---- this lane's rotated, pre-scaled query in B-operand order: step s
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     // causal: keys up to the workgroup's last query; otherwise every key, the
     // windows applying to |i - j|
-    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
+    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
     // key tiles of this workgroup's split of the key range: [kt0, kt1)
     const int sp = blockIdx.y;
@@ -570,7 +577,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     {                                                                                      \
         const int j0_ = (kt_) * KT;                                                        \
         const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
-                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QT - 1))); \
+                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QS - 1))); \
         const int c_min_ = 2 * (cut_below(win, dmin_wg_) >> 3);                            \
         /* a key chunk below c_min is not fetched: its offset is past the buffer's end */ \
         unsigned koff_[KPER];                                                              \
@@ -912,20 +919,24 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const int xcd = L & 7, slot = L >> 3;
     const int gi = (slot / a.group) * 8 + xcd;
     if (gi >= a.n_groups) return;
-    const int hg = slot % a.group;
+    const int hs = slot % a.group;  // head in the group, or (head packed) slab of NW heads
     const int per_qt = a.B * a.Hkv;
     const int qt = a.n_qtiles - 1 - gi / per_qt;
     const int rem = gi % per_qt;
     const int b = rem / a.Hkv, hk = rem % a.Hkv;
-    const int h = hk * a.group + hg;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = lane & 15, g = lane >> 4;
-    const int i0 = qt * QT + wave * 16;
+    // as in the 32x32 kernel: QT rows of one head, or 16 rows of NW heads
+    const int hgroup = a.Hq / a.Hkv;
+    const int hw = a.hpack ? NW * hs + wave : 0;
+    const int h = a.hpack ? hk * hgroup + min(hw, hgroup - 1) : hk * a.group + hs;
+    const int QS = a.hpack ? 16 : QT;
+    const int i0 = a.hpack ? qt * 16 : qt * QT + wave * 16;
     const int my_q = i0 + t;
-    const bool q_valid = my_q < a.Sq;
+    const bool q_valid = my_q < a.Sq && hw < hgroup;
     const int qoff = (int)(a.q_pos0 - a.k_pos0);
-    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QT + qoff;
+    const int i0k = i0 + qoff, my_qk = my_q + qoff, q0k = qt * QS + qoff;
     const WaveWin<P> win = load_windows<P>(a.W);
     const int kbase_g = 16 * (g >> 1) + 4 * (g & 1);  // key of slot (sb 0, r 0) in a block
 
@@ -958,7 +969,7 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
 
     const unsigned char *kg = (const unsigned char *)a.krot + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
-    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QT - 1) : a.Sk - 1;
+    const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
     // key tiles of this workgroup's split of the key range: [kt0, kt1)
     const int sp = blockIdx.y;
@@ -981,7 +992,7 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     {                                                                                      \
         const int j0_ = (kt_) * KT;                                                        \
         const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
-                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QT - 1))); \
+                                    : max(0, max(q0k - (j0_ + KT - 1), j0_ - (q0k + QS - 1))); \
         const int c_min_ = cut_below(win, dmin_wg_) >> 2;                                  \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kg + (long long)j0_ * (D * 2), KT_BYTES); \
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \

@@ -163,6 +163,10 @@ def test_chunk_workspace_sizes(lib):
     assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 32768, 128, atf.ATF_F32) == 256
     assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 200, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 200, 128, atf.ATF_BF16)
+    # 7 heads per kv head, 16 queries: head-packed work items (one per kv head)
+    # leave 4 workgroups with work, so 64 splits; unpacked it would be 28 (18 splits)
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 131072, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + 28 * 16 * 64 * 130 * 4
     # d = 256: 64-key tiles, 128-query tiles
     assert atf.atf_prefill_chunk_workspace_bytes(1, 2, 1, 100, 1500, 256, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + 2 * 100 * 11 * 258 * 4

@@ -190,3 +190,34 @@ def test_chunk_short_after_long_prefix(env, d):
     dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, q_pos0=Sk - Sq, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, dense, "chunk short after long prefix d=%d" % d)
     assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,rows", [(128, 8, 1, 32), (256, 16, 2, 16)])
+def test_chunk_head_packed_matches_unpacked(env, d, Hq, Hkv, rows):
+    """A chunk of one wave's rows runs head packed (one wave per query head of
+    a kv group); a 1024-query chunk ending at the same token runs unpacked.
+    The shared rows form the same wave blocks over the same key tiles, so
+    they agree bit for bit (minimum workspace: no key split)."""
+    torch, oracle, atf, inputs = env
+    dev = torch.device("cuda:0")
+    Sk, base, alpha = 3000, 1e6, 1.0
+    log("case: chunk head packed vs unpacked d=%d" % d)
+    q, k, v = inputs.make_qkv(1, Hq, Hkv, 1024, Sk, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(atf.atf_prefill_workspace_bytes(1, Hkv, Sk, d, atf.ATF_BF16), dtype=torch.uint8, device=dev)
+    full = atf.atf_prefill_chunk(q, k, v, rope_base=base, alpha=alpha, ws=ws)
+    tail = atf.atf_prefill_chunk(q[:, :, 1024 - rows:].contiguous(), k, v, rope_base=base, alpha=alpha, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(tail, full[:, :, 1024 - rows:])
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,d", [(16, 1, 40, 128), (12, 1, 33, 128), (24, 2, 20, 256), (5, 1, 7, 64)])
+def test_chunk_head_packed_slabs(env, Hq, Hkv, Sq, d):
+    """Head-packed chunks with more heads per kv head than waves (two slabs,
+    the second partly idle) or fewer (idle waves), against the oracle."""
+    torch, oracle, atf, _ = env
+    Sk, base, alpha = 2500, 1e6, 1.0
+    log("case: chunk head packed Hq=%d Hkv=%d Sq=%d d=%d" % (Hq, Hkv, Sq, d))
+    q, k, v, out, skipped = run_chunk(env, 1, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "chunk head packed %s" % ((Hq, Hkv, Sq, d),))
+    assert skipped == ref_skipped
