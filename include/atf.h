@@ -186,6 +186,66 @@ atf_status atf_prefill_chunk(const void *q, const void *k, const void *v, void *
                              atf_dtype dtype, void *workspace, size_t workspace_bytes,
                              uint64_t *skipped_out, atf_stream_t stream);
 
+/* --------------------------------------------- prefill over a kept key cache */
+
+/*
+ * A prefill key cache: the form atf_prefill_prepare_kv writes (keys rotated
+ * once at their positions, pair-interleaved; values transposed per 64-key
+ * tile), kept across calls so that a chunked prefill rotates only its own
+ * new keys.  Same method as atf_prefill_chunk (source page "ATFlash: ..."
+ * (sudo-ai.de), section "Die Zahlen - und ihre Grenze": the windows drop
+ * into the prefill path unchanged, a chunk is that path with a query
+ * offset); only where the keys come from differs.  bf16 only.
+ *
+ * Layout, for capacity S_cap keys per (b, kv head), S_pad = S_cap rounded up
+ * to 128: rotated keys [B][Hkv][S_pad][d], then values [B][Hkv][S_pad / 64]
+ * [d][64] (bf16).  Key j sits at position pos0 + j.  The caller owns the
+ * cache; calls on one cache are ordered by their stream.
+ */
+size_t atf_prefill_cache_bytes(int32_t B, int32_t Hkv, int64_t S_cap, int32_t d);
+
+/*
+ * Writes keys k_begin .. k_begin + n - 1 of the cache from k, v
+ * [B][Hkv][n][d] (pre-RoPE, bf16; row r is key k_begin + r at position
+ * pos0 + k_begin + r).  Keys before k_begin are kept.  The cache then holds
+ * k_begin + n keys: the keys after them up to the end of their 128-key tile
+ * are cleared, so an append must not start inside a longer filled prefix it
+ * means to keep.  rope_layout is that of k (and of the q later attending).
+ * Errors: n < 1, k_begin < 0 or k_begin + n > S_cap is ATF_ERR_INVALID_ARG;
+ * cache_bytes < atf_prefill_cache_bytes(...) is ATF_ERR_WORKSPACE; shape and
+ * argument rules as atf_prefill_prepare_kv with S = S_cap.
+ */
+atf_status atf_prefill_cache_append(const void *k, const void *v, int32_t B, int32_t Hkv, int64_t n,
+                                    int64_t k_begin, int64_t S_cap, int32_t d, int32_t rope_layout,
+                                    double rope_base, int64_t pos0, void *cache, size_t cache_bytes,
+                                    atf_stream_t stream);
+
+/*
+ * Scratch bytes for atf_prefill_chunk_cached: 256 (the dropped-term counter)
+ * plus, when the planner splits the key range, B*Hq*Sq*n_split rows of d + 2
+ * floats of partials (n_split <= 64).  0 for rejected shapes.
+ */
+size_t atf_prefill_cached_scratch_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d);
+
+/*
+ * Chunked prefill over the first Sk keys of a cache: q, out [B][Hq][Sq][d]
+ * bf16 are the last Sq of those Sk tokens (query i at position
+ * pos0 + Sk - Sq + i), as atf_prefill_chunk with the same k, v would see
+ * them; the result equals atf_prefill_chunk's bit for bit when both run with
+ * the same split (the same scratch or workspace size class).  Keys 0 .. Sk - 1
+ * must have been appended.  `scratch` (device, >= 256 bytes, 16-byte
+ * aligned) takes the counter; with atf_prefill_cached_scratch_bytes(...)
+ * bytes or more it also takes the split partials.  Calls that share a
+ * scratch buffer must be ordered.  Errors: Sq < 1, Sq > Sk or Sk > S_cap is
+ * ATF_ERR_INVALID_ARG; a short cache or scratch is ATF_ERR_WORKSPACE; other
+ * rules as atf_prefill_chunk.
+ */
+atf_status atf_prefill_chunk_cached(const void *q, void *out, int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq,
+                                    int64_t Sk, int64_t S_cap, int32_t d, int32_t rope_layout, double rope_base,
+                                    double alpha, int32_t causal, int64_t pos0, const void *cache,
+                                    size_t cache_bytes, void *scratch, size_t scratch_bytes,
+                                    uint64_t *skipped_out, atf_stream_t stream);
+
 /* ------------------------------------------------------------------- decode */
 
 /* Bytes of workspace atf_decode needs (per-split partial results + counter). */

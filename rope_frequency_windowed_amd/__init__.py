@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     atf_decode_kcache_bytes, atf_decode_pack_k, atf_decode_paged, atf_decode_paged_workspace_bytes,
     atf_decode_workspace_bytes, atf_paged_page_bytes,
     atf_paged_write, atf_prefill, atf_prefill_attend, atf_prefill_chunk, atf_prefill_chunk_workspace_bytes,
+    atf_prefill_cache_append, atf_prefill_cache_bytes, atf_prefill_cached_scratch_bytes, atf_prefill_chunk_cached,
     atf_prefill_prepare_kv,
     atf_prefill_workspace_bytes, atf_skipped_pair_products, atf_version, atf_window_table,
     library, workspace,

@@ -26,7 +26,8 @@ EXPORTED = (
     "atf_status_string", "atf_version", "atf_window_table", "atf_skipped_pair_products",
     "atf_prefill_workspace_bytes", "atf_prefill", "atf_prefill_prepare_kv",
     "atf_prefill_attend", "atf_prefill_chunk", "atf_prefill_chunk_workspace_bytes",
-    "atf_decode_workspace_bytes", "atf_decode",
+    "atf_prefill_cache_bytes", "atf_prefill_cache_append", "atf_prefill_cached_scratch_bytes",
+    "atf_prefill_chunk_cached", "atf_decode_workspace_bytes", "atf_decode",
     "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
     "atf_paged_page_bytes", "atf_decode_paged_workspace_bytes", "atf_paged_write", "atf_decode_paged",
 )
@@ -76,6 +77,15 @@ def _lib():
     lib.atf_prefill_chunk.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f64, f64, i32, i64,
                                       ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_prefill_chunk.restype = ctypes.c_int
+    lib.atf_prefill_cache_bytes.argtypes = [i32, i32, i64, i32]
+    lib.atf_prefill_cache_bytes.restype = sz
+    lib.atf_prefill_cache_append.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, i32, f64, i64, vp, sz, vp]
+    lib.atf_prefill_cache_append.restype = ctypes.c_int
+    lib.atf_prefill_cached_scratch_bytes.argtypes = [i32, i32, i32, i64, i64, i32]
+    lib.atf_prefill_cached_scratch_bytes.restype = sz
+    lib.atf_prefill_chunk_cached.argtypes = [vp, vp, i32, i32, i32, i64, i64, i64, i32, i32, f64, f64, i32, i64,
+                                             vp, sz, vp, sz, u64p, vp]
+    lib.atf_prefill_chunk_cached.restype = ctypes.c_int
     lib.atf_decode_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
     lib.atf_decode_workspace_bytes.restype = sz
     lib.atf_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i32, i32, f64, f64, i32, i64,
@@ -140,6 +150,50 @@ def atf_prefill_workspace_bytes(B: int, Hkv: int, S: int, d: int, dtype: int) ->
 
 def atf_prefill_chunk_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, dtype: int) -> int:
     return int(_lib().atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, dtype))
+
+
+def atf_prefill_cache_bytes(B: int, Hkv: int, S_cap: int, d: int) -> int:
+    return int(_lib().atf_prefill_cache_bytes(B, Hkv, S_cap, d))
+
+
+def atf_prefill_cached_scratch_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int) -> int:
+    return int(_lib().atf_prefill_cached_scratch_bytes(B, Hq, Hkv, Sq, Sk, d))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def atf_prefill_cache_append(k, v, cache, *, k_begin: int, cap: int, rope_base: float, pos0: int = 0,
+                             rope_layout="neox"):
+    """Write k, v [B,Hkv,n,d] (pre-RoPE, bf16) as keys k_begin .. k_begin+n-1
+    of a prefill cache of capacity `cap` (a uint8 buffer of
+    atf_prefill_cache_bytes bytes)."""
+    B, Hkv, n, d = k.shape
+    _check(_lib().atf_prefill_cache_append(_dev(k, "k"), _dev(v, "v"), B, Hkv, n, int(k_begin), int(cap), d,
+                                           _layout_code(rope_layout), float(rope_base), int(pos0),
+                                           _dev(cache, "cache"), _nbytes(cache), _stream(k.device)),
+           "atf_prefill_cache_append")
+
+
+def atf_prefill_chunk_cached(q, cache, out=None, *, Hkv: int, Sk: int, cap: int, rope_base: float, alpha: float,
+                             causal: int = 1, pos0: int = 0, scratch=None, return_skipped: bool = False,
+                             rope_layout="neox"):
+    """Chunked prefill over the first Sk keys of a prefill cache: q [B,Hq,Sq,d]
+    are the last Sq of those Sk tokens (query i at pos0+Sk-Sq+i)."""
+    B, Hq, Sq, d = q.shape
+    if out is None:
+        out = _torch().empty_like(q)
+    if scratch is None:
+        scratch = workspace(atf_prefill_cached_scratch_bytes(B, Hq, Hkv, Sq, Sk, d), q.device, "prefill_scratch")
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_prefill_chunk_cached(_dev(q, "q"), _dev(out, "out"), B, Hq, Hkv, Sq, int(Sk), int(cap), d,
+                                           _layout_code(rope_layout), float(rope_base), float(alpha), int(causal),
+                                           int(pos0), _dev(cache, "cache"), _nbytes(cache),
+                                           _dev(scratch, "scratch"), _nbytes(scratch),
+                                           ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_prefill_chunk_cached")
+    return (out, int(skipped.value)) if return_skipped else out
 
 
 def atf_decode_workspace_bytes(B: int, Hq: int, Hkv: int, S: int, d: int) -> int:

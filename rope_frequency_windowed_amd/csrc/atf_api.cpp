@@ -121,6 +121,12 @@ int chunk_ksplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int
     return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, max_by_keys), kMaxKSplit));
 }
 
+// Prefill key cache (bf16): rotated keys, then transposed values, both laid
+// out for S_cap keys per (b, kv head), as in the prepared workspace.
+size_t pcache_bytes(int32_t B, int32_t Hkv, int64_t S_cap, int32_t d) {
+    return 2 * (size_t)B * Hkv * (size_t)padded_keys(S_cap) * d * 2;
+}
+
 size_t chunk_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
     const int ns = chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, dtype);
     const size_t part = ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0;
@@ -233,29 +239,33 @@ atf_status read_counter(unsigned long long *dev, uint64_t *host, hipStream_t s) 
     return ATF_OK;
 }
 
-// Attention over keys already prepared in the workspace: Sq query rows that
-// sit at key indices Sk - Sq .. Sk - 1 (positions pos0 + Sk - Sq + i), Sk keys
-// at positions pos0 + j.  Shapes are checked by the caller.
-atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
+// Where a bf16 attention call finds its prepared keys and values.
+struct KvView {
+    const void *krot, *vt;
+    int64_t S_pad;  // keys per (b, kv head) in krot and vt
+};
+
+// Attention over prepared keys: Sq query rows that sit at key indices
+// Sk - Sq .. Sk - 1 (positions pos0 + Sk - Sq + i), Sk keys at positions
+// pos0 + j.  fp32 reads raw k and v; bf16 reads `kv`.  The count goes to
+// `counter` (cleared here); a key-range split (n_ksplit > 1) writes its
+// partials to `part`.  Shapes and buffers are checked by the caller.
+atf_status attend_core(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
                        int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, int32_t layout, double rope_base, double alpha,
-                       int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
-                       uint64_t *skipped_out, hipStream_t s, int n_ksplit = 1) {
-    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
-    if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
-    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
-        return ATF_ERR_WORKSPACE;
+                       int32_t causal, int64_t pos0, atf_dtype dtype, const KvView &kv,
+                       unsigned long long *counter, float *part, int n_ksplit, uint64_t *skipped_out,
+                       hipStream_t s) {
     AttnArgs a;
     std::memset(&a, 0, sizeof(a));
     a.q = q;
     a.out = out;
-    a.counter = (unsigned long long *)workspace;
+    a.counter = counter;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.group = Hq / Hkv;
     a.Sq = (int)Sq;
     a.Sk = (int)Sk;
-    a.Sk_pad = (int)padded_keys(Sk);
     a.q_pos0 = pos0 + (Sk - Sq);
     a.k_pos0 = pos0;
     a.causal = causal;
@@ -263,7 +273,7 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
-    // the count is per call: clear it (the prepared workspace may be reused)
+    // the count is per call: clear it (the prepared keys may be reused)
     hipError_t e = launch_fill_zero_u64(a.counter, s);
     if (e != hipSuccess) return ATF_ERR_HIP;
     if (dtype == ATF_F32) {
@@ -273,22 +283,38 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
         a.Sk_pad = (int)Sk;
         e = launch_attend_f32(a, d, s);
     } else {
-        char *ws = (char *)workspace + kHeaderBytes;
-        const size_t per = (size_t)B * Hkv * (size_t)a.Sk_pad * d * 2;
-        a.krot = ws;
-        a.vt = ws + per;
+        a.krot = kv.krot;
+        a.vt = kv.vt;
+        a.Sk_pad = (int)kv.S_pad;
         const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
         a.hpack = pl.hpack;
         a.n_qtiles = pl.n_qtiles;
         a.group = pl.group;
         a.n_groups = a.n_qtiles * B * Hkv;
         a.n_ksplit = n_ksplit;
-        // partials of a key-range split follow the prepared keys and values
-        a.part = n_ksplit > 1 ? (float *)((char *)workspace + prefill_ws_bytes(B, Hkv, Sk, d, dtype)) : nullptr;
+        a.part = n_ksplit > 1 ? part : nullptr;
         e = launch_prefill_bf16(a, d, s);
     }
     if (e != hipSuccess) return ATF_ERR_HIP;
     return read_counter(a.counter, skipped_out, s);
+}
+
+// attend_core over the workspace of atf_prefill_prepare_kv: counter in the
+// header, then K' and V^T for Sk keys, then (split) the partials.
+atf_status attend_impl(const void *q, const void *k, const void *v, void *out, int32_t B, int32_t Hq,
+                       int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, int32_t layout, double rope_base, double alpha,
+                       int32_t causal, int64_t pos0, atf_dtype dtype, void *workspace, size_t workspace_bytes,
+                       uint64_t *skipped_out, hipStream_t s, int n_ksplit = 1) {
+    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype == ATF_F32 && (!aligned16(k) || !aligned16(v))) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || workspace_bytes < prefill_ws_bytes(B, Hkv, Sk, d, dtype))
+        return ATF_ERR_WORKSPACE;
+    char *ws = (char *)workspace + kHeaderBytes;
+    const int64_t S_pad = padded_keys(Sk);
+    const KvView kv{ws, ws + (size_t)B * Hkv * (size_t)S_pad * d * 2, S_pad};
+    float *part = (float *)((char *)workspace + prefill_ws_bytes(B, Hkv, Sk, d, dtype));
+    return attend_core(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, layout, rope_base, alpha, causal, pos0, dtype, kv,
+                       (unsigned long long *)workspace, part, n_ksplit, skipped_out, s);
 }
 
 }  // namespace
@@ -362,6 +388,10 @@ atf_status atf_prefill_prepare_kv(const void *k, const void *v, int32_t B, int32
     a.Hkv = Hkv;
     a.S = (int)S;
     a.S_pad = (int)padded_keys(S);
+    a.k_begin = 0;
+    a.k_end = a.src_rows = (int)S;
+    a.tile0 = 0;
+    a.n_tiles = a.S_pad / kKeyTile;
     a.pos0 = pos0;
     a.gptj = rope_layout;
     theta_table(d, rope_base, a.theta);
@@ -429,6 +459,73 @@ size_t atf_prefill_chunk_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sq > Sk || (!supported_d(d))) return 0;
     if (dtype != ATF_F32 && dtype != ATF_BF16) return 0;
     return chunk_ws_bytes(B, Hq, Hkv, Sq, Sk, d, dtype);
+}
+
+size_t atf_prefill_cache_bytes(int32_t B, int32_t Hkv, int64_t S_cap, int32_t d) {
+    if (B < 1 || Hkv < 1 || S_cap < 1 || padded_keys(S_cap) >= (int64_t)INT32_MAX || (!supported_d(d))) return 0;
+    return pcache_bytes(B, Hkv, S_cap, d);
+}
+
+atf_status atf_prefill_cache_append(const void *k, const void *v, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
+                                    int64_t S_cap, int32_t d, int32_t rope_layout, double rope_base, int64_t pos0,
+                                    void *cache, size_t cache_bytes, atf_stream_t stream) {
+    if (n < 1 || k_begin < 0 || k_begin > S_cap - n) return ATF_ERR_INVALID_ARG;
+    atf_status st = check_shape(B, Hkv, Hkv, S_cap, d, rope_base, 1.0, 1, pos0, ATF_BF16);
+    if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(cache) || cache_bytes < pcache_bytes(B, Hkv, S_cap, d)) return ATF_ERR_WORKSPACE;
+    PrepArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = k;
+    a.v = v;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.S = (int)S_cap;
+    a.S_pad = (int)padded_keys(S_cap);
+    a.k_begin = (int)k_begin;
+    a.k_end = (int)(k_begin + n);
+    a.src_rows = (int)n;
+    // from the tile holding k_begin to the end of the attention tile holding
+    // the last key: the keys after it in that tile are cleared
+    a.tile0 = (int)(k_begin / kKeyTile);
+    a.n_tiles = (int)(std::min<int64_t>(a.S_pad, padded_keys(k_begin + n)) / kKeyTile) - a.tile0;
+    a.pos0 = pos0;
+    a.gptj = rope_layout;
+    theta_table(d, rope_base, a.theta);
+    char *c = (char *)cache;
+    a.krot = c;
+    a.vt = c + pcache_bytes(B, Hkv, S_cap, d) / 2;
+    return hip_status(launch_prep_bf16(a, d, (hipStream_t)stream));
+}
+
+size_t atf_prefill_cached_scratch_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sq > Sk || (!supported_d(d))) return 0;
+    const int ns = chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, ATF_BF16);
+    return kHeaderBytes + (ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0);
+}
+
+atf_status atf_prefill_chunk_cached(const void *q, void *out, int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq,
+                                    int64_t Sk, int64_t S_cap, int32_t d, int32_t rope_layout, double rope_base,
+                                    double alpha, int32_t causal, int64_t pos0, const void *cache,
+                                    size_t cache_bytes, void *scratch, size_t scratch_bytes, uint64_t *skipped_out,
+                                    atf_stream_t stream) {
+    if (Sq < 1 || Sq > Sk || Sk > S_cap) return ATF_ERR_INVALID_ARG;
+    atf_status st = check_shape(B, Hq, Hkv, S_cap, d, rope_base, alpha, causal, pos0, ATF_BF16);
+    if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(cache) || cache_bytes < pcache_bytes(B, Hkv, S_cap, d)) return ATF_ERR_WORKSPACE;
+    if (!aligned16(scratch) || scratch_bytes < kHeaderBytes) return ATF_ERR_WORKSPACE;
+    // split the key range when the scratch has room for the partials
+    const int ns = scratch_bytes >= atf_prefill_cached_scratch_bytes(B, Hq, Hkv, Sq, Sk, d)
+                       ? chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, ATF_BF16) : 1;
+    const int64_t S_pad = padded_keys(S_cap);
+    const char *c = (const char *)cache;
+    const KvView kv{c, c + pcache_bytes(B, Hkv, S_cap, d) / 2, S_pad};
+    return attend_core(q, nullptr, nullptr, out, B, Hq, Hkv, Sq, Sk, d, rope_layout, rope_base, alpha, causal, pos0,
+                       ATF_BF16, kv, (unsigned long long *)scratch, (float *)((char *)scratch + kHeaderBytes), ns,
+                       skipped_out, (hipStream_t)stream);
 }
 
 size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {

@@ -41,8 +41,10 @@ struct PrepArgs {
     const void *v;
     void *krot;                       // rotated keys [B][Hkv][S_pad][d]
     void *vt;                         // bf16 only: transposed value tiles
-    unsigned long long *counter;      // zeroed here
-    int B, Hkv, S, S_pad;
+    unsigned long long *counter;      // zeroed here (nullable)
+    int B, Hkv, S, S_pad;             // S: fp32 rows; S_pad: keys per (b, h) in krot / vt
+    int k_begin, k_end, src_rows;     // bf16: keys [k_begin, k_end) from src_rows rows per (b, h)
+    int tile0, n_tiles;               // bf16: 64-key tiles written: [tile0, tile0 + n_tiles)
     long long pos0;
     int gptj;                         // rotary pairs: 0 = dims (p, p + d/2), 1 = dims (2p, 2p + 1)
     double theta[kMaxPairs];

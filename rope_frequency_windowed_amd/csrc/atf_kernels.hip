@@ -148,7 +148,10 @@ constexpr int kswz_rows() { return (CH >= 16) ? 16 : 8; }  // period of kswz in 
 // (dims (p, p+P) side by side as one 32-bit word), and store the values
 // transposed per 64-key tile, keys permuted inside each group of 16 so that
 // the attention kernel's MFMA operand for P.V is one 16-byte LDS read.
-// grid (S_pad/64, B*Hkv), block 256.
+// Keys [k_begin, k_end) come from source rows 0 .. k_end - k_begin - 1; keys
+// past k_end are cleared, keys before k_begin (the first tile of an append
+// that does not start on a tile) are kept.
+// grid (number of 64-key tiles from tile0, B*Hkv), block 256.
 // ============================================================================
 
 // Key held at position `pos` (0..15) of a 16-key group of a value tile.
@@ -161,20 +164,21 @@ template <int D>
 __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
     constexpr int P = D / 2;
     constexpr int PPT = P / 4;  // pairs per thread (16 or 8)
-    const int tile = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-    const unsigned short *k = (const unsigned short *)a.k + (long long)bh * a.S * D;
-    const unsigned short *v = (const unsigned short *)a.v + (long long)bh * a.S * D;
+    const int tile = a.tile0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    // source rows: key j is row j - k_begin
+    const unsigned short *k = (const unsigned short *)a.k + (long long)bh * a.src_rows * D;
+    const unsigned short *v = (const unsigned short *)a.v + (long long)bh * a.src_rows * D;
     unsigned *kr = (unsigned *)a.krot + (long long)bh * a.S_pad * P;
     unsigned short *vt = (unsigned short *)a.vt + ((long long)bh * (a.S_pad / kKeyTile) + tile) * (D * kKeyTile);
 
-    if (tile == 0 && bh == 0 && t == 0) *a.counter = 0ull;
+    if (a.counter && blockIdx.x == 0 && bh == 0 && t == 0) *a.counter = 0ull;
 
     {  // keys
         const int row = t >> 2, p0 = (t & 3) * PPT;
         const int j = tile * kKeyTile + row;
         union { u32x4 v[PPT / 4]; unsigned w[PPT]; } res;
-        if (j < a.S) {
-            const unsigned short *src = k + (long long)j * D;
+        if (j >= a.k_begin && j < a.k_end) {
+            const unsigned short *src = k + (long long)(j - a.k_begin) * D;
             const long long pos = a.pos0 + j;
             u32x2 lo[PPT / 4], hi[PPT / 4];
 #pragma unroll
@@ -191,8 +195,10 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
             for (int u = 0; u < PPT; ++u) res.w[u] = 0u;
         }
         u32x4 *dst = (u32x4 *)(kr + (long long)j * P + p0);
+        if (j >= a.k_begin) {
 #pragma unroll
-        for (int u = 0; u < PPT / 4; ++u) dst[u] = res.v[u];
+            for (int u = 0; u < PPT / 4; ++u) dst[u] = res.v[u];
+        }
     }
 
     {  // values: tile [64][D] -> LDS -> [D][64] with the in-group key permutation
@@ -205,20 +211,23 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
             const int row = g / CHR, ch = g % CHR;
             const int j = tile * kKeyTile + row;
             u32x4 val = (u32x4){0u, 0u, 0u, 0u};
-            if (j < a.S) val = *(const u32x4 *)(v + (long long)j * D + ch * 8);
+            if (j >= a.k_begin && j < a.k_end) val = *(const u32x4 *)(v + (long long)(j - a.k_begin) * D + ch * 8);
             *(u32x4 *)(vs + row * LD + ch * 8) = val;
         }
         __syncthreads();
+        const int keep = a.k_begin - tile * kKeyTile;  // keys of this tile already in place
 #pragma unroll
         for (int n = 0; n < (D * 8) / 256; ++n) {
             const int g = t + 256 * n;
             const int dim = g >> 3, pc = g & 7;
-            union { u32x4 v; unsigned short s[8]; } o;
+            union { u32x4 v; unsigned short s[8]; } o, old;
+            old.v = (u32x4){0u, 0u, 0u, 0u};
+            if (keep > 0) old.v = *(const u32x4 *)(vt + dim * kKeyTile + pc * 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int pos = pc * 8 + e;
                 const int key = (pos & ~15) + vt_key_of_pos(pos & 15);
-                o.s[e] = vs[key * LD + dim];
+                o.s[e] = key < keep ? old.s[e] : vs[key * LD + dim];
             }
             *(u32x4 *)(vt + dim * kKeyTile + pc * 8) = o.v;
         }
@@ -2264,7 +2273,7 @@ __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s) {
-    dim3 grid((unsigned)(a.S_pad / kKeyTile), (unsigned)(a.B * a.Hkv));
+    dim3 grid((unsigned)a.n_tiles, (unsigned)(a.B * a.Hkv));
     if (d == 256) prep_bf16_kernel<256><<<grid, 256, 0, s>>>(a);
     else if (d == 128) prep_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else prep_bf16_kernel<64><<<grid, 256, 0, s>>>(a);

@@ -339,3 +339,82 @@ def test_probe_library_exports_and_checks_arguments():
     assert lib.atf_probe_mfma_bf16(16, 32, 0, 1, None) == 1
     assert lib.atf_probe_hbm_read(16, 100, 32, 1, None) == 1      # size not a multiple of 256 KiB
     assert lib.atf_probe_hbm_read(8, 1 << 18, 32, 1, None) == 1   # misaligned
+
+
+def test_prefill_cache_sizes(lib):
+    assert atf.atf_prefill_cache_bytes(1, 4, 3000, 128) == 2 * 4 * 3072 * 128 * 2
+    assert atf.atf_prefill_cache_bytes(2, 1, 128, 64) == 2 * 2 * 128 * 64 * 2
+    assert atf.atf_prefill_cache_bytes(1, 4, 3000, 96) == 0
+    assert atf.atf_prefill_cache_bytes(1, 4, 0, 128) == 0
+    # scratch: counter, plus the partials of the same split the chunk call plans
+    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 16, 131072, 128) == 256 + 28 * 16 * 64 * 130 * 4
+    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 32768, 32768, 128) == 256
+    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 17, 16, 128) == 0
+    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 3, 16, 100, 128) == 0
+    for args in ((1, 28, 4, 16, 131072, 128), (1, 2, 1, 100, 1500, 256), (1, 4, 4, 16, 1000, 128)):
+        B, Hq, Hkv, Sq, Sk, d = args
+        assert atf.atf_prefill_cached_scratch_bytes(*args) - 256 == \
+            atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16) - \
+            atf.atf_prefill_workspace_bytes(B, Hkv, Sk, d, atf.ATF_BF16)
+
+
+def _call_append(lib, **kw):
+    args = dict(k=16, v=32, B=1, Hkv=2, n=64, k_begin=0, cap=1000, d=128, layout=0, base=1e6, pos0=0,
+                cache=4096, cache_bytes=1, stream=None)
+    args.update(kw)
+    return lib.atf_prefill_cache_append(ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["v"]), args["B"],
+                                        args["Hkv"], args["n"], args["k_begin"], args["cap"], args["d"],
+                                        args["layout"], args["base"], args["pos0"], ctypes.c_void_p(args["cache"]),
+                                        args["cache_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), bnd.ATF_ERR_WORKSPACE),                   # valid: stops at the cache size
+    (dict(n=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(k_begin=-1), bnd.ATF_ERR_INVALID_ARG),
+    (dict(k_begin=937), bnd.ATF_ERR_INVALID_ARG),      # k_begin + n > cap
+    (dict(k_begin=936), bnd.ATF_ERR_WORKSPACE),        # ends exactly at cap
+    (dict(k=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(v=8), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(layout=3), bnd.ATF_ERR_INVALID_ARG),
+    (dict(base=0.5), bnd.ATF_ERR_INVALID_ARG),
+    (dict(cache=None), bnd.ATF_ERR_WORKSPACE),
+    (dict(pos0=(1 << 31) - 500), bnd.ATF_ERR_INVALID_ARG),
+])
+def test_cache_append_rejects(lib, kw, expect):
+    assert _call_append(lib, **kw) == expect
+
+
+def _call_cached(lib, **kw):
+    args = dict(q=16, out=32, B=1, Hq=4, Hkv=2, Sq=64, Sk=500, cap=1000, d=128, layout=0, base=1e6, alpha=1.0,
+                causal=1, pos0=0, cache=4096, cache_bytes=2 * 2 * 1024 * 128 * 2, scratch=8192, scratch_bytes=1,
+                skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_prefill_chunk_cached(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["out"]), args["B"],
+                                        args["Hq"], args["Hkv"], args["Sq"], args["Sk"], args["cap"], args["d"],
+                                        args["layout"], args["base"], args["alpha"], args["causal"], args["pos0"],
+                                        ctypes.c_void_p(args["cache"]), args["cache_bytes"],
+                                        ctypes.c_void_p(args["scratch"]), args["scratch_bytes"], args["skipped"],
+                                        args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), bnd.ATF_ERR_WORKSPACE),                   # valid: stops at the scratch size
+    (dict(Sq=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(Sq=501), bnd.ATF_ERR_INVALID_ARG),           # Sq > Sk
+    (dict(Sk=1001), bnd.ATF_ERR_INVALID_ARG),          # Sk > cap
+    (dict(Hq=5), bnd.ATF_ERR_INVALID_ARG),
+    (dict(q=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(out=40), bnd.ATF_ERR_INVALID_ARG),
+    (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG),
+    (dict(causal=3), bnd.ATF_ERR_INVALID_ARG),
+    (dict(layout=5), bnd.ATF_ERR_INVALID_ARG),
+    (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(cache_bytes=2 * 2 * 1024 * 128 * 2 - 1), bnd.ATF_ERR_WORKSPACE),
+    (dict(cache=None), bnd.ATF_ERR_WORKSPACE),
+    (dict(scratch=None, scratch_bytes=256), bnd.ATF_ERR_WORKSPACE),
+    (dict(scratch_bytes=255), bnd.ATF_ERR_WORKSPACE),
+])
+def test_chunk_cached_rejects(lib, kw, expect):
+    assert _call_cached(lib, **kw) == expect
