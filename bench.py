@@ -173,7 +173,8 @@ def time_leg(torch, stream, fn, steps):
 def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     """Decode at the main decode size with GPT-J interleaved pairs (standard
     [S][d] cache); prefill at S=32K, at 128K with alpha 0.5 and 2, and at 1M;
-    a 4096-token chunk after a 126976-token prefix; non-causal prefill at 32K;
+    a 4096-token chunk after a 126976-token prefix; a 16-token chunk step over
+    a kept 131072-key prefill cache; non-causal prefill at 32K;
     prefill/decode with 256-dim heads."""
     out = {}
     D = DECODE
@@ -243,6 +244,39 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     log("prefill chunk Sq=%d after %d cached: %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
         % (Sq, Sk - Sq, ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
     del q, k, v, o, ws
+
+    # a serving step over a kept prefill cache: append 16 new keys (rotated and
+    # laid out once), then attend their queries over all 131072 keys (key
+    # split and head packing); same dropped-term count rule as above
+    Sq = 16
+    q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], Sq, Sk, d, dtype=torch.bfloat16, device=dev)
+    o = torch.empty_like(q)
+    cache = torch.empty(atf.atf_prefill_cache_bytes(P["B"], P["Hkv"], Sk, d), dtype=torch.uint8, device=dev)
+    atf.atf_prefill_cache_append(k, v, cache, k_begin=0, cap=Sk, rope_base=P["base"])
+    kn, vn = k[:, :, Sk - Sq:].contiguous(), v[:, :, Sk - Sq:].contiguous()
+    scratch = torch.empty(atf.atf_prefill_cached_scratch_bytes(P["B"], P["Hq"], P["Hkv"], Sq, Sk, d),
+                          dtype=torch.uint8, device=dev)
+
+    def cached_step(return_skipped=False):
+        atf.atf_prefill_cache_append(kn, vn, cache, k_begin=Sk - Sq, cap=Sk, rope_base=P["base"])
+        return atf.atf_prefill_chunk_cached(q, cache, o, Hkv=P["Hkv"], Sk=Sk, cap=Sk, rope_base=P["base"],
+                                            alpha=P["alpha"], scratch=scratch, return_skipped=return_skipped)
+    _, got = cached_step(True)
+    per_head = (atf.atf_skipped_pair_products(Sk, d, P["base"], P["alpha"]) -
+                atf.atf_skipped_pair_products(Sk - Sq, d, P["base"], P["alpha"]))
+    if got != P["B"] * P["Hq"] * per_head:
+        raise SystemExit("cached chunk dropped-term count differs from the closed form")
+    ms = time_leg(torch, stream, cached_step, steps)
+    n_c = Sq * (Sk - Sq) + Sq * (Sq + 1) // 2
+    flops = P["B"] * P["Hq"] * (4 * (d // 2) * n_c + 2 * d * n_c) - 4 * got
+    tf = flops / (ms * 1e-3) / 1e12
+    out["prefill_chunk_cached_sq16"] = {
+        "value": P["B"] * Sq / (ms * 1e-3), "unit": "tok/s (append 16 keys to the kept cache, attend the chunk)",
+        "ms": ms, "config": dict(P, S=None, Sq=Sq, Sk=Sk),
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops}}
+    log("prefill chunk Sq=%d over a kept %d-key cache: %.3f ms" % (Sq, Sk, ms))
+    del q, k, v, o, cache, kn, vn, scratch
 
     # non-causal windows (|i - j| against W_p), S=32K
     P = dict(PREFILL, S=32768)
