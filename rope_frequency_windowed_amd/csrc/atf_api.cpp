@@ -93,16 +93,22 @@ size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype 
 // rows of one head (a wave per 32 rows, 16 at d = 256).  Head packed: one
 // wave's rows of up to 8 heads sharing a kv head, so a short chunk does not
 // run mostly empty tiles (a 16-query chunk fills 1/16 of a 256-row tile).
-// Packed when it runs fewer wave rows (its idle waves included).
+// Packed when it runs fewer wave rows (its idle waves included).  A d = 128
+// chunk of at most 16 queries runs packed on the 16x16x32 kernel (narrow),
+// whose 16-query waves carry no empty rows there.
 struct PrefillPlan {
     int hpack, n_qtiles, group;  // group: heads per kv head, or (packed) slabs of 8 heads
+    int narrow;                  // d = 128 on the 16x16x32 kernel
 };
 PrefillPlan prefill_plan(int32_t Hq, int32_t Hkv, int64_t Sq, int32_t d) {
-    const int64_t qt = prefill_query_tile(d), rows = d == 256 ? 16 : 32, nw = qt / rows;
+    const int narrow = d == 128 && Sq <= 16;
+    const bool k16 = d == 256 || narrow;  // the 16x16x32 kernel
+    const int64_t rows = k16 ? 16 : 32, nw = k16 ? kPrefill16Waves : kPrefillWaves;
+    const int64_t qt = rows * nw;
     const int group = Hq / Hkv, slabs = (int)((group + nw - 1) / nw);
     const int64_t n_tiles = (Sq + qt - 1) / qt, n_blocks = (Sq + rows - 1) / rows;
-    if (n_blocks * rows * slabs * nw * Hkv < n_tiles * qt * Hq) return {1, (int)n_blocks, slabs};
-    return {0, (int)n_tiles, group};
+    if (narrow || n_blocks * rows * slabs * nw * Hkv < n_tiles * qt * Hq) return {1, (int)n_blocks, slabs, narrow};
+    return {0, (int)n_tiles, group, 0};
 }
 
 // Key-range splits of a chunked prefill (bf16).  A small chunk has few query
@@ -115,7 +121,7 @@ int chunk_ksplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int
     if (dtype != ATF_BF16) return 1;
     const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
     const int64_t active = (int64_t)pl.n_qtiles * B * Hkv * pl.group;  // workgroups with work
-    const int64_t kt = d == 256 ? kPrefill16Keys : kPrefillKeys;
+    const int64_t kt = (d == 256 || pl.narrow) ? kPrefill16Keys : kPrefillKeys;
     const int64_t max_by_keys = std::max<int64_t>(1, Sk / kt / 2);
     const int64_t want = 512 / active;
     return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, max_by_keys), kMaxKSplit));
@@ -288,6 +294,7 @@ atf_status attend_core(const void *q, const void *k, const void *v, void *out, i
         a.Sk_pad = (int)kv.S_pad;
         const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
         a.hpack = pl.hpack;
+        a.narrow = pl.narrow;
         a.n_qtiles = pl.n_qtiles;
         a.group = pl.group;
         a.n_groups = a.n_qtiles * B * Hkv;

@@ -65,6 +65,7 @@ struct AttnArgs {
     int n_qtiles, n_groups;           // work decomposition
     int n_ksplit;                     // key-range splits (grid.y); > 1: partials to `part`, then a combine
     int hpack;                        // 1: a work item is one query block of up to 8 heads sharing a kv head
+    int narrow;                       // 1: d = 128 on the 16x16x32 kernel (16-query waves)
     float *part;                      // [B*Hq*Sq][n_ksplit][d + 2]  (o..., m, l), n_ksplit > 1 only
     float scale_log2;                 // log2(e) / sqrt(d)
     int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)

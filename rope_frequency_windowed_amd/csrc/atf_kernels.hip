@@ -2291,6 +2291,9 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     if (d == 256) {
         if (a.causal) prefill16_bf16_kernel<256, true><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
         else prefill16_bf16_kernel<256, false><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
+    } else if (a.narrow) {  // d = 128, at most 16 queries: 16-query waves
+        if (a.causal) prefill16_bf16_kernel<128, true><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
+        else prefill16_bf16_kernel<128, false><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
     } else if (a.causal) {
         if (d == 128) prefill_bf16_kernel<128, true><<<grid, kPrefillWaves * 64, 0, s>>>(a);
         else prefill_bf16_kernel<64, true><<<grid, kPrefillWaves * 64, 0, s>>>(a);

@@ -155,8 +155,8 @@ def test_chunk_workspace_sizes(lib):
     assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 32768, 128, atf.ATF_BF16) == \
         pre + 4 * 16 * 64 * 130 * 4
     # at most Sk / 256 splits (two 128-key tiles each)
-    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 1000, 128, atf.ATF_BF16) == \
-        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 4 * 16 * 3 * 130 * 4
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 17, 1000, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 4 * 17 * 3 * 130 * 4
     # a chunk that fills the GPU by itself, fp32, or a too-short key range: no partials
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 32768, 32768, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 32768, 128, atf.ATF_BF16)
@@ -167,6 +167,12 @@ def test_chunk_workspace_sizes(lib):
     # leave 4 workgroups with work, so 64 splits; unpacked it would be 28 (18 splits)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 131072, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + 28 * 16 * 64 * 130 * 4
+    # at most 16 queries (d = 128): 64-key tiles of the 16x16x32 kernel, so
+    # Sk = 1000 allows 7 splits of two tiles (128-key tiles would allow 3)
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 1000, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 28 * 16 * 7 * 130 * 4
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 17, 1000, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 28 * 17 * 3 * 130 * 4
     # d = 256: 64-key tiles, 128-query tiles
     assert atf.atf_prefill_chunk_workspace_bytes(1, 2, 1, 100, 1500, 256, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + 2 * 100 * 11 * 258 * 4
@@ -351,7 +357,7 @@ def test_prefill_cache_sizes(lib):
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 32768, 32768, 128) == 256
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 17, 16, 128) == 0
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 3, 16, 100, 128) == 0
-    for args in ((1, 28, 4, 16, 131072, 128), (1, 2, 1, 100, 1500, 256), (1, 4, 4, 16, 1000, 128)):
+    for args in ((1, 28, 4, 16, 131072, 128), (1, 2, 1, 100, 1500, 256), (1, 4, 4, 17, 1000, 128)):
         B, Hq, Hkv, Sq, Sk, d = args
         assert atf.atf_prefill_cached_scratch_bytes(*args) - 256 == \
             atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16) - \

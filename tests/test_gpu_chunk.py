@@ -221,3 +221,23 @@ def test_chunk_head_packed_slabs(env, Hq, Hkv, Sq, d):
     ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, None, "chunk head packed %s" % ((Hq, Hkv, Sq, d),))
     assert skipped == ref_skipped
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,Sk,causal", [
+    (28, 4, 16, 9000, 1), (7, 1, 5, 3001, 1), (16, 1, 1, 2000, 1), (28, 4, 16, 5000, 0), (8, 2, 9, 300, 1)])
+def test_chunk_narrow_d128(env, Hq, Hkv, Sq, Sk, causal):
+    """d = 128 chunks of at most 16 queries run head packed on the 16x16x32
+    kernel (16-query waves), with the key split; against the oracle."""
+    torch, oracle, atf, _ = env
+    base, alpha = 1e6, 1.0
+    log("case: chunk narrow d=128 %s" % ((Hq, Hkv, Sq, Sk, causal),))
+    dev = torch.device("cuda:0")
+    from rope_frequency_windowed_amd import inputs
+    q, k, v = inputs.make_qkv(1, Hq, Hkv, Sq, Sk, 128, dtype=torch.bfloat16, device=dev)
+    out, skipped = atf.atf_prefill_chunk(q, k, v, rope_base=base, alpha=alpha, causal=causal, return_skipped=True)
+    torch.cuda.synchronize()
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, causal=bool(causal), q_pos0=Sk - Sq,
+                                        k_pos0=0)
+    dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, causal=bool(causal), q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, dense, "chunk narrow %s" % ((Hq, Hkv, Sq, Sk, causal),))
+    assert skipped == ref_skipped
