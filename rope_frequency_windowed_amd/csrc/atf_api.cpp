@@ -89,13 +89,13 @@ size_t prefill_ws_bytes(int32_t B, int32_t Hkv, int64_t S, int32_t d, atf_dtype 
     return kHeaderBytes + 2 * per;  // rotated keys + transposed values
 }
 
-// bf16 prefill work items.  Unpacked: a query tile of prefill_query_tile(d)
-// rows of one head (a wave per 32 rows, 16 at d = 256).  Head packed: one
-// wave's rows of up to 8 heads sharing a kv head, so a short chunk does not
-// run mostly empty tiles (a 16-query chunk fills 1/16 of a 256-row tile).
-// Packed when it runs fewer wave rows (its idle waves included).  A d = 128
-// chunk of at most 16 queries runs packed on the 16x16x32 kernel (narrow),
-// whose 16-query waves carry no empty rows there.
+// bf16 prefill work items.  Unpacked: a query tile of 8 waves' rows of one
+// head (32 rows per wave; 16 on the 16x16x32 kernel, which runs d = 256).
+// Head packed: one wave's rows of up to 8 heads sharing a kv head, so a short
+// chunk does not run mostly empty tiles (a 16-query chunk fills 1/16 of a
+// 256-row tile).  Packed when it runs fewer wave rows (its idle waves
+// included).  A d = 128 chunk of at most 16 queries runs packed on the
+// 16x16x32 kernel (narrow), whose 16-query waves carry no empty rows there.
 struct PrefillPlan {
     int hpack, n_qtiles, group;  // group: heads per kv head, or (packed) slabs of 8 heads
     int narrow;                  // d = 128 on the 16x16x32 kernel

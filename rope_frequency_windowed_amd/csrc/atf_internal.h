@@ -23,9 +23,6 @@ constexpr int kPrefillKeys = ATF_PREFILL_KEYS;         // keys per LDS tile
 // queries fit two per SIMD.  64-key tiles keep the double buffer at 128 KB.
 constexpr int kPrefill16Waves = 8;
 constexpr int kPrefill16Keys = 64;
-constexpr int prefill_query_tile(int d) {  // queries per workgroup (bf16)
-    return d == 256 ? 16 * kPrefill16Waves : 32 * kPrefillWaves;
-}
 constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
 constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
 constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves
