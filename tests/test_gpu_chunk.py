@@ -241,3 +241,19 @@ def test_chunk_narrow_d128(env, Hq, Hkv, Sq, Sk, causal):
     dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, causal=bool(causal), q_pos0=Sk - Sq, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, dense, "chunk narrow %s" % ((Hq, Hkv, Sq, Sk, causal),))
     assert skipped == ref_skipped
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d", [(3, 8, 2, 20, 2000, 128), (2, 14, 2, 8, 3000, 128),
+                                              (2, 6, 3, 40, 1500, 64), (2, 16, 2, 10, 1200, 256)])
+def test_chunk_split_packed_batch(env, B, Hq, Hkv, Sq, Sk, d):
+    """Key split with head-packed (and, for 8 queries at d = 128, narrow) work
+    items over several sequences: the partials and work items index by batch."""
+    torch, oracle, atf, _ = env
+    base, alpha = 1e6, 1.0
+    log("case: chunk split packed batch %s" % ((B, Hq, Hkv, Sq, Sk, d),))
+    assert atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16) > \
+        atf.atf_prefill_workspace_bytes(B, Hkv, Sk, d, atf.ATF_BF16)
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "chunk split packed batch %s" % ((B, Hq, Hkv, Sq, Sk, d),))
+    assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
