@@ -1767,15 +1767,59 @@ __device__ inline int paged_nsplit(const DecodeArgs &a, int b) {
 
 // Algorithmic bytes of keys [0, j) of a sequence of S keys (decode query after
 // them): 2d per value row plus 4 per kept pair, where pair p (finite W_p) is
-// dropped for the keys j' < S - W_p.  Every lane returns the sum.
-template <int D>
-__device__ inline long long dec_prefix_bytes(int j, int S, const WaveWin<D / 2> &win) {
-    constexpr int P = D / 2;
+// dropped for the keys j' < S - W_p, i.e. sum_p min(j, max(0, S - W_p))
+// dropped pair-keys.  The windows are sorted, so with p1 = #{W_p <= S - j} and
+// p2 = #{W_p < S} that sum is j p1 + sum_{p1 <= p < p2} (S - W_p): two ballot
+// counts and a prefix table of the windows, no cross-lane sums.
+template <int P>
+struct WinPrefix {      // lane l: sum of the finite windows of pairs below l (and below 64 + l)
+    long long lo, hi;
+};
+template <int P>
+__device__ inline WinPrefix<P> win_prefix(const WaveWin<P> &win) {
     const int lane = threadIdx.x & 63;
-    long long dropped = 0;
-    if (lane < P - 1 && win.lo != kWindowInf) dropped = min(j, max(0, S - win.lo));
-    if (P > 64 && lane + 64 < P - 1 && win.hi != kWindowInf) dropped += min(j, max(0, S - win.hi));
-    dropped = (long long)wave_sum_u64((unsigned long long)dropped);
+    auto excl_scan = [&](int w) {
+        const long long v = (w != kWindowInf) ? (long long)w : 0ll;
+        long long incl = v;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const long long y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        return incl - v;
+    };
+    WinPrefix<P> r;
+    r.lo = excl_scan(win.lo);
+    r.hi = 0;
+    if constexpr (P > 64) {
+        const long long last = __shfl(r.lo, 63, 64) + (win.lo != kWindowInf ? (long long)__shfl(win.lo, 63, 64) : 0ll);
+        r.hi = last + excl_scan(win.hi);
+    }
+    return r;
+}
+// sum of the finite windows of pairs [0, p), p wave-uniform
+template <int P>
+__device__ inline long long win_prefix_at(const WinPrefix<P> &pw, const WaveWin<P> &win, int p) {
+    auto rl = [](long long v, int l) {
+        const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, l);
+        const unsigned hi = __builtin_amdgcn_readlane((unsigned)((unsigned long long)v >> 32), l);
+        return (long long)(((unsigned long long)hi << 32) | lo);
+    };
+    if (p < 64) return rl(pw.lo, p);
+    if constexpr (P > 64) {
+        if (p < 128) return rl(pw.hi, p - 64);
+        const int w = __builtin_amdgcn_readlane(win.hi, 63);
+        return rl(pw.hi, 63) + (w != kWindowInf ? (long long)w : 0ll);
+    }
+    const int w = __builtin_amdgcn_readlane(win.lo, 63);
+    return rl(pw.lo, 63) + (w != kWindowInf ? (long long)w : 0ll);
+}
+template <int D>
+__device__ inline long long dec_prefix_bytes(int j, int S, const WaveWin<D / 2> &win, const WinPrefix<D / 2> &pw) {
+    constexpr int P = D / 2;
+    const int p1 = cut_below(win, S - j + 1), p2 = cut_below(win, S);  // the infinite window never counts
+    const long long dropped = (long long)j * p1 + (long long)(p2 - p1) * S -
+                              (win_prefix_at<P>(pw, win, p2) - win_prefix_at<P>(pw, win, p1));
     return (long long)j * (2 * D + 4 * P) - 4 * dropped;
 }
 
@@ -1969,14 +2013,15 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         // planner): split s of nsb starts at the first 64-key chunk whose
         // prefix of algorithmic bytes reaches s / nsb of the total; splits past
         // nsb have no keys
-        const long long total = dec_prefix_bytes<D>(S, S, win);
+        const WinPrefix<P> pw = win_prefix<P>(win);
+        const long long total = dec_prefix_bytes<D>(S, S, win, pw);
         const int nchunks = (S + kKeyTile - 1) / kKeyTile;
         auto start_of = [&](int sp) {
             const long long target = total * min(sp, nsb) / nsb;
             int lo = 0, hi = nchunks;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
-                if (dec_prefix_bytes<D>(min(S, mid * kKeyTile), S, win) < target) lo = mid + 1; else hi = mid;
+                if (dec_prefix_bytes<D>(min(S, mid * kKeyTile), S, win, pw) < target) lo = mid + 1; else hi = mid;
             }
             return lo * kKeyTile;
         };
