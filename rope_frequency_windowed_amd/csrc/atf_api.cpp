@@ -166,9 +166,13 @@ int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
     return (int)std::max<int64_t>(ns, 1);
 }
 
+// Decode workspace: header (counter), the rotated queries ([B*Hq][d/2] bf16
+// pair words, rounded up to 256 bytes), then the split partials.
+size_t dec_qrot_bytes(int32_t B, int32_t Hq, int32_t d) { return ((size_t)B * Hq * d * 2 + 255) / 256 * 256; }
+
 size_t decode_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
     const int ns = decode_nsplit(B, Hq, Hkv, S, d);
-    return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
+    return kHeaderBytes + dec_qrot_bytes(B, Hq, d) + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
 // Paged, ragged decode: the batch shares a budget of ~512 workgroups per call
@@ -187,7 +191,7 @@ void paged_plan(int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, int &budget
 size_t paged_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d) {
     int budget, ns;
     paged_plan(Hq, Hkv, max_len, d, budget, ns);
-    return kHeaderBytes + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
+    return kHeaderBytes + dec_qrot_bytes(B, Hq, d) + (size_t)B * Hq * ns * (size_t)(d + 2) * sizeof(float);
 }
 
 // Algorithmic bytes of keys [0, j) for a query at distance S - j' from key j':
@@ -585,7 +589,8 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out, in
     a.v = v;
     a.out = out;
     a.counter = counter;
-    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.qrot = (unsigned *)((char *)workspace + kHeaderBytes);
+    a.part = (float *)((char *)workspace + kHeaderBytes + dec_qrot_bytes(B, Hq, d));
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -659,7 +664,8 @@ atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, v
     a.v = v;
     a.out = out;
     a.counter = (unsigned long long *)workspace;
-    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.qrot = (unsigned *)((char *)workspace + kHeaderBytes);
+    a.part = (float *)((char *)workspace + kHeaderBytes + dec_qrot_bytes(B, Hq, d));
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -750,7 +756,8 @@ atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool,
     a.v = vpool;
     a.out = out;
     a.counter = (unsigned long long *)workspace;
-    a.part = (float *)((char *)workspace + kHeaderBytes);
+    a.qrot = (unsigned *)((char *)workspace + kHeaderBytes);
+    a.part = (float *)((char *)workspace + kHeaderBytes + dec_qrot_bytes(B, Hq, d));
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;

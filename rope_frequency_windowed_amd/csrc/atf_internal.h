@@ -75,6 +75,7 @@ struct DecodeArgs {
     const void *k;
     const void *v;
     float *part;                      // [B*Hq][nsplit][d + 2]  (o..., m, l)
+    unsigned *qrot;                   // bf16: [B*Hq][d/2] rotated, scaled query pair words
     void *out;
     unsigned long long *counter;
     int B, Hq, Hkv, group, S, nsplit, n_slabs;

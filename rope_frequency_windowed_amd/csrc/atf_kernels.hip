@@ -1406,7 +1406,6 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char *lds, unsigned byte_ad
 template <int D, bool GPTJ>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
-    constexpr bool QGPTJ = GPTJ;  // rotary layout of q and k
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
     constexpr int CK = 32;               // keys per wave chunk
@@ -1429,7 +1428,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const int nh = min(H, a.group - slab * H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int t = lane & 15, q = lane >> 4;
-    const long long qpos = a.pos0 + a.S;
 
     for (int e = tid; e < P * CK; e += 256) {
         const int p = e / CK, u = e % CK;
@@ -1445,27 +1443,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const WaveWin<P> win = load_windows<P>(a.W);
 
     // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
-    // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
+    // as decode_qrot_kernel rotated and scaled them; empty slots are 0
     bf16x8_t qf[NSTEP];
     {
-        const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + t) * D;
+        const unsigned *qrow = a.qrot + (long long)(b * a.Hq + h0 + t) * P;
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-            if (t < nh) {
-                const int pb = 16 * s + 4 * q;
-                u32x2 lo, hi;
-                load_pair_pieces(qrow, pb, P, QGPTJ, lo, hi);
-                unsigned r[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float x, y, c, sn;
-                    pair_xy(lo, hi, u, QGPTJ, x, y);
-                    rope_cos_sin(qpos, a.theta[pb + u], c, sn);
-                    r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
-                }
-                w = (u32x4){r[0], r[1], r[2], r[3]};
-            }
+            if (t < nh) w = *(const u32x4 *)(qrow + 16 * s + 4 * q);
             qf[s] = __builtin_bit_cast(bf16x8_t, w);
         }
     }
@@ -1916,7 +1901,6 @@ __global__ __launch_bounds__(256) void paged_write_bf16_kernel(PagedWriteArgs a)
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
-    const bool QGPTJ = a.gptj != 0;  // rotary layout of q (keys are stored rotated)
     constexpr int P = D / 2;
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
@@ -1976,32 +1960,18 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
     const int t = lane & 15, q = lane >> 4;
     // keys of this sequence (ragged when paged: clamped to [1, a.S], a.S = max_len)
     const int S = PAGED ? min(max(a.seq_lens[b], 1), a.S) : a.S;
-    const long long qpos = a.pos0 + S;
 
     const WaveWin<P> win = load_windows<P>(a.W);
 
     // query operand (B of the score MFMA): head slot t, pairs 16s + 4q + (0..3),
-    // rotated at the query position and scaled by log2(e)/sqrt(d); empty slots are 0
+    // as decode_qrot_kernel rotated and scaled them; empty slots are 0
     bf16x8_t qf[NSTEP];
     {
-        const unsigned short *qrow = (const unsigned short *)a.q + (long long)(b * a.Hq + h0 + t) * D;
+        const unsigned *qrow = a.qrot + (long long)(b * a.Hq + h0 + t) * P;
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
             u32x4 w = (u32x4){0u, 0u, 0u, 0u};
-            if (t < nh) {
-                const int pb = 16 * s + 4 * q;
-                u32x2 lo, hi;
-                load_pair_pieces(qrow, pb, P, QGPTJ, lo, hi);
-                unsigned r[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    float x, y, c, sn;
-                    pair_xy(lo, hi, u, QGPTJ, x, y);
-                    rope_cos_sin(qpos, a.theta[pb + u], c, sn);
-                    r[u] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
-                }
-                w = (u32x4){r[0], r[1], r[2], r[3]};
-            }
+            if (t < nh) w = *(const u32x4 *)(qrow + 16 * s + 4 * q);
             qf[s] = __builtin_bit_cast(bf16x8_t, w);
         }
     }
@@ -2313,6 +2283,34 @@ __global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
 
 __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
 
+// The decode queries, rotated once per call at their position (pos0 + S, or
+// pos0 + seq_lens[b] when paged) and scaled by log2(e)/sqrt(d): word p of row
+// b*Hq + h is (x'_p, x'_{p+P}) in bf16, the score MFMA's operand order, so the
+// split kernels load their query operand instead of each rotating it.  Also
+// clears the dropped-term counter.  grid B*Hq, block P.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(D / 2) void decode_qrot_kernel(DecodeArgs a) {
+    constexpr int P = D / 2;
+    const int row = blockIdx.x, p = threadIdx.x;
+    if (row == 0 && p == 0) *a.counter = 0ull;
+    const int b = row / a.Hq;
+    const int S = PAGED ? min(max(a.seq_lens[b], 1), a.S) : a.S;
+    const unsigned short *qrow = (const unsigned short *)a.q + (long long)row * D;
+    const int ix = a.gptj ? 2 * p : p, iy = a.gptj ? 2 * p + 1 : p + P;
+    const float x = __uint_as_float((unsigned)qrow[ix] << 16), y = __uint_as_float((unsigned)qrow[iy] << 16);
+    float c, sn;
+    rope_cos_sin(a.pos0 + S, a.theta[p], c, sn);
+    a.qrot[(long long)row * P + p] = pack_bf((x * c - y * sn) * a.scale_log2, (y * c + x * sn) * a.scale_log2);
+}
+
+template <bool PAGED>
+void launch_decode_qrot(const DecodeArgs &a, int d, hipStream_t s) {
+    const unsigned rows = (unsigned)(a.B * a.Hq);
+    if (d == 256) decode_qrot_kernel<256, PAGED><<<rows, 128, 0, s>>>(a);
+    else if (d == 128) decode_qrot_kernel<128, PAGED><<<rows, 64, 0, s>>>(a);
+    else decode_qrot_kernel<64, PAGED><<<rows, 32, 0, s>>>(a);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
@@ -2364,7 +2362,7 @@ hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
-    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    launch_decode_qrot<false>(a, d, s);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
     if (d == 256 && a.gptj) decode_bf16_kernel<256, true><<<grid, 256, 0, s>>>(a);
     else if (d == 256) decode_bf16_kernel<256, false><<<grid, 256, 0, s>>>(a);
@@ -2401,7 +2399,7 @@ hipError_t launch_paged_write_bf16(const PagedWriteArgs &a, int d, hipStream_t s
 }
 
 hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s) {
-    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    launch_decode_qrot<true>(a, d, s);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
     // paged: x walks the batch's splits (at most budget + B of them), y = (kv head, slab)
     grid = dim3((unsigned)(a.split_budget + a.B), (unsigned)(a.Hkv * a.n_slabs));
@@ -2417,7 +2415,7 @@ hipError_t launch_decode_paged_bf16(const DecodeArgs &a, int d, hipStream_t s) {
 }
 
 hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) {
-    fill_zero_u64_kernel<<<1, 1, 0, s>>>(a.counter);
+    launch_decode_qrot<false>(a, d, s);
     dim3 grid((unsigned)a.nsplit, (unsigned)(a.B * a.Hkv * a.n_slabs));
     if (d == 256) decode_kcache_bf16_kernel<256, false><<<grid, 256, 0, s>>>(a);
     else if (d == 128) decode_kcache_bf16_kernel<128, false><<<grid, 256, 0, s>>>(a);

@@ -143,9 +143,11 @@ def test_workspace_sizes(lib):
     assert atf.atf_prefill_workspace_bytes(1, 4, 100, 128, atf.ATF_BF16) == 256 + 2 * 4 * 128 * 128 * 2
     assert atf.atf_prefill_workspace_bytes(1, 1, 256, 64, atf.ATF_F32) == 256
     assert atf.atf_prefill_workspace_bytes(1, 1, 256, 96, atf.ATF_BF16) == 0
+    # header, rotated queries (B*Hq rows of d bf16, rounded up to 256 bytes), partials
     ws = atf.atf_decode_workspace_bytes(8, 28, 4, 262144, 128)
-    assert ws == 256 + 8 * 28 * 16 * 130 * 4  # 512 workgroups over 32 (sequence, kv head) units
-    assert atf.atf_decode_workspace_bytes(1, 1, 1, 10, 128) == 256 + 1 * 1 * 1 * 130 * 4
+    assert ws == 256 + 8 * 28 * 128 * 2 + 8 * 28 * 16 * 130 * 4  # 512 workgroups over 32 (sequence, kv head) units
+    assert atf.atf_decode_workspace_bytes(1, 1, 1, 10, 128) == 256 + 256 + 1 * 1 * 1 * 130 * 4
+    assert atf.atf_decode_workspace_bytes(1, 3, 1, 10, 64) == 256 + 512 + 3 * 1 * 66 * 4
     assert atf.atf_decode_workspace_bytes(1, 3, 2, 10, 128) == 0
 
 
