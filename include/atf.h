@@ -248,7 +248,9 @@ atf_status atf_prefill_chunk_cached(const void *q, void *out, int32_t B, int32_t
 
 /* ------------------------------------------------------------------- decode */
 
-/* Bytes of workspace atf_decode needs (per-split partial results + counter). */
+/* Bytes of workspace atf_decode and atf_decode_kcache need: the counter, the
+ * queries rotated once per call (B*Hq*d bf16), and the per-split partial
+ * results. */
 size_t atf_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d);
 
 /*
@@ -336,9 +338,9 @@ atf_status atf_decode_kcache(const void *q, const void *kcache, const void *v, v
  * 0 for unsupported Hkv or d. */
 size_t atf_paged_page_bytes(int32_t Hkv, int32_t d);
 
-/* Bytes of workspace atf_decode_paged needs (per-split partials sized for the
- * widest split count one sequence of max_len tokens can take, + counter);
- * 0 for unsupported shapes. */
+/* Bytes of workspace atf_decode_paged needs (counter, rotated queries, and
+ * per-split partials sized for the widest split count one sequence of max_len
+ * tokens can take); 0 for unsupported shapes. */
 size_t atf_decode_paged_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d);
 
 /*
