@@ -224,8 +224,8 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     Sq, Sk, d = 4096, 131072, P["d"]
     q, k, v = make_qkv(P["B"], P["Hq"], P["Hkv"], Sq, Sk, d, dtype=torch.bfloat16, device=dev)
     o = torch.empty_like(q)
-    ws = torch.empty(atf.atf_prefill_workspace_bytes(P["B"], P["Hkv"], Sk, d, atf.ATF_BF16), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(atf.atf_prefill_chunk_workspace_bytes(P["B"], P["Hq"], P["Hkv"], Sq, Sk, d, atf.ATF_BF16),
+                     dtype=torch.uint8, device=dev)
     _, got = atf.atf_prefill_chunk(q, k, v, o, rope_base=P["base"], alpha=P["alpha"], ws=ws, return_skipped=True)
     per_head = (atf.atf_skipped_pair_products(Sk, d, P["base"], P["alpha"]) -
                 atf.atf_skipped_pair_products(Sk - Sq, d, P["base"], P["alpha"]))

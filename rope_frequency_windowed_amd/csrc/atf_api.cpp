@@ -122,9 +122,22 @@ int chunk_ksplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int
     const PrefillPlan pl = prefill_plan(Hq, Hkv, Sq, d);
     const int64_t active = (int64_t)pl.n_qtiles * B * Hkv * pl.group;  // workgroups with work
     const int64_t kt = (d == 256 || pl.narrow) ? kPrefill16Keys : kPrefillKeys;
-    const int64_t max_by_keys = std::max<int64_t>(1, Sk / kt / 2);
-    const int64_t want = 512 / active;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, max_by_keys), kMaxKSplit));
+    const int64_t cap = std::min<int64_t>(std::max<int64_t>(1, Sk / kt / 2), kMaxKSplit);
+    if (active <= 256) return (int)std::max<int64_t>(1, std::min<int64_t>(512 / active, cap));
+    // More than one round of resident workgroups (one per CU), the last maybe
+    // part-full.  When every query tile walks about the same key range (a
+    // chunk after a prefix of at least three times its length), split so the
+    // rounds come out fuller: the split count with the fewest rounds per unit
+    // of work, kept only if it saves at least 5% (the partials' traffic).
+    if (Sk < 4 * Sq) return 1;
+    constexpr int64_t kResident = 256;
+    auto rounds_per_work = [&](int64_t ns) {
+        return (double)((active * ns + kResident - 1) / kResident) / (double)ns;
+    };
+    int64_t best = 1;
+    for (int64_t ns = 2; ns <= std::min<int64_t>(cap, 8); ++ns)
+        if (rounds_per_work(ns) < 0.95 * rounds_per_work(best)) best = ns;
+    return (int)best;
 }
 
 // Prefill key cache (bf16): rotated keys, then transposed values, both laid

@@ -169,6 +169,13 @@ def test_chunk_workspace_sizes(lib):
     # leave 4 workgroups with work, so 64 splits; unpacked it would be 28 (18 splits)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 131072, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + 28 * 16 * 64 * 130 * 4
+    # 4096 queries after 126976 cached tokens: 448 query-tile workgroups fill
+    # 1.75 rounds of 256; four splits make 7 full rounds
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 4096, 131072, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + 28 * 4096 * 4 * 130 * 4
+    # the same queries over a prefix shorter than three chunks: no split
+    assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 4096, 16000, 128, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(1, 4, 16000, 128, atf.ATF_BF16)
     # at most 16 queries (d = 128): 64-key tiles of the 16x16x32 kernel, so
     # Sk = 1000 allows 7 splits of two tiles (128-key tiles would allow 3)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 1000, 128, atf.ATF_BF16) == \
