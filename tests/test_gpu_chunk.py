@@ -257,3 +257,18 @@ def test_chunk_split_packed_batch(env, B, Hq, Hkv, Sq, Sk, d):
     ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, None, "chunk split packed batch %s" % ((B, Hq, Hkv, Sq, Sk, d),))
     assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
+
+
+def test_chunk_full_round_split(env):
+    """270 query-tile workgroups (just over one round of 256) after a prefix of
+    more than three chunks: the planner splits the key range in two so the
+    rounds come out full; every row against the oracle."""
+    torch, oracle, atf, _ = env
+    B, Hq, Hkv, Sq, Sk, d, base, alpha = 3, 90, 90, 100, 520, 64, 1e4, 1.0
+    log("case: chunk full-round split %s" % ((B, Hq, Hkv, Sq, Sk, d),))
+    assert atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16) == \
+        atf.atf_prefill_workspace_bytes(B, Hkv, Sk, d, atf.ATF_BF16) + B * Hq * Sq * 2 * (d + 2) * 4
+    q, k, v, out, skipped = run_chunk(env, B, Hq, Hkv, Sq, Sk, d, base, alpha, torch.bfloat16)
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, None, "chunk full-round split")
+    assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
