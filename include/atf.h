@@ -38,7 +38,7 @@
  *     is the caller's `workspace` (size from the *_workspace_bytes query).
  *   - Errors are status codes only; nothing throws or aborts.  Every argument
  *     check runs on the host before anything is queued.
- *   - Supported: d in {64, 128}; Hq % Hkv == 0; Hq/Hkv <= 64; S >= 1;
+ *   - Supported: d in {64, 128, 256}; Hq % Hkv == 0; Hq/Hkv <= 64; S >= 1;
  *     0 <= pos0 and pos0 + S + 1 < 2^31; alpha > 0 (finite or +inf; +inf
  *     means no window); rope_base > 1 and finite; causal in {0, 1}.
  *   - rope_layout (calls that read q or k rows): ATF_ROPE_NEOX or

@@ -230,14 +230,26 @@ def _stream(device):
 
 
 _WS = {}
+_WS_RETIRED = []
 
 
 def workspace(nbytes: int, device, tag: str):
-    """A cached caller-owned workspace of at least nbytes on `device`."""
+    """A cached caller-owned workspace of at least nbytes on `device`, one per
+    (device, stream, tag): calls queued on different streams never share
+    scratch.  A buffer outgrown by a later call is kept alive (never freed),
+    so work already queued on it still owns its memory.  Under HIP graph
+    capture the cache is not used: the caller must pass its own buffer, whose
+    lifetime it controls for as long as the graph may replay."""
     torch = _torch()
-    key = (str(device), tag)
+    if torch.device(device).type != "cuda":
+        raise ValueError("tensors must be GPU tensors")
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("no default workspace under graph capture: pass ws= / scratch= explicitly")
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream, tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _WS_RETIRED.append(ws)
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
