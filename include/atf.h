@@ -374,6 +374,35 @@ atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool,
                             atf_dtype dtype, void *workspace, size_t workspace_bytes,
                             uint64_t *skipped_out, atf_stream_t stream);
 
+/* ------------------------------------------------ decode that allocates nothing */
+
+/* Bytes of the library's own device scratch array (one per GPU, held from the
+ * library's first use on that GPU until the process ends). */
+#define ATF_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * atf_decode_paged for callers that cannot allocate or own a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and results as atf_decode_paged
+ * (bit-identical outputs, same kernels) without workspace/workspace_bytes:
+ * the counter, rotated queries and split partials live in the library's
+ * static device array of ATF_NOALLOC_SCRATCH_BYTES on the current GPU.  The
+ * caller still owns q, out, the pools and the arrays.  Nothing is allocated
+ * (no hipMalloc, hipFree or allocating library call).
+ * Limit: shapes with atf_decode_paged_workspace_bytes(B, Hq, Hkv, max_len, d)
+ * > ATF_NOALLOC_SCRATCH_BYTES are ATF_ERR_WORKSPACE, checked on the host
+ * before any HIP call (e.g. Hq = 28, Hkv = 4, d = 128: B <= 17).
+ * `stream` must belong to the current device (else ATF_ERR_INVALID_ARG).
+ * Every call on one GPU shares that GPU's array and leaves it holding its
+ * partials: calls that overlap on one GPU (different streams, or several host
+ * threads) race and give wrong results; order them on one stream.
+ */
+atf_status atf_decode_paged_noalloc(const void *q, const void *kpool, const void *vpool, void *out,
+                                    const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
+                                    int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len,
+                                    int32_t d, int32_t rope_layout, double rope_base, double alpha, int32_t causal,
+                                    int64_t pos0, atf_dtype dtype, uint64_t *skipped_out, atf_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

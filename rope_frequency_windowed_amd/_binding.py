@@ -30,7 +30,9 @@ EXPORTED = (
     "atf_prefill_chunk_cached", "atf_decode_workspace_bytes", "atf_decode",
     "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
     "atf_paged_page_bytes", "atf_decode_paged_workspace_bytes", "atf_paged_write", "atf_decode_paged",
+    "atf_decode_paged_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATF_NOALLOC_SCRATCH_BYTES
 
 
 class AtfError(RuntimeError):
@@ -109,6 +111,9 @@ def _lib():
                                      i64,
                                      ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode_paged.restype = ctypes.c_int
+    lib.atf_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i64, i32, i32, f64,
+                                             f64, i32, i64, ctypes.c_int, u64p, vp]
+    lib.atf_decode_paged_noalloc.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -446,6 +451,31 @@ def atf_decode_paged(q, kpool, vpool, page_table, seq_lens, out=None, *, max_len
                                    int(causal), int(pos0), code, _dev(ws, "workspace"), ws.numel(),
                                    ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
            "atf_decode_paged")
+    return (out, int(skipped.value)) if return_skipped else out
+
+
+def atf_decode_paged_noalloc(q, kpool, vpool, page_table, seq_lens, out=None, *, max_len: int, rope_base: float,
+                             alpha: float, causal: int = 1, pos0: int = 0, return_skipped: bool = False,
+                             rope_layout="neox"):
+    """atf_decode_paged with the library's own scratch (no workspace): for
+    callers that cannot allocate.  Calls that overlap on one GPU race."""
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query per sequence")
+    max_pages = page_table.shape[1]
+    if kpool.dim() < 2:
+        raise ValueError("kpool must be shaped [num_pages, Hkv, ...]")
+    Hkv, num_pages = kpool.shape[1], kpool.shape[0]
+    if out is None:
+        out = _torch().empty_like(q)
+    skipped = ctypes.c_uint64(0)
+    _check(_lib().atf_decode_paged_noalloc(_dev(q, "q"), _dev(kpool, "kpool"), _dev(vpool, "vpool"),
+                                           _dev(out, "out"), _dev_i32(page_table, "page_table"),
+                                           _dev_i32(seq_lens, "seq_lens"), max_pages, num_pages, B, Hq, Hkv,
+                                           int(max_len), d, _layout_code(rope_layout), float(rope_base),
+                                           float(alpha), int(causal), int(pos0), _dtype_code(q),
+                                           ctypes.byref(skipped) if return_skipped else None, _stream(q.device)),
+           "atf_decode_paged_noalloc")
     return (out, int(skipped.value)) if return_skipped else out
 
 

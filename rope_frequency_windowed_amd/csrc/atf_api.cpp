@@ -17,6 +17,8 @@
 #include <cstring>
 #include <vector>
 
+static_assert((size_t)ATF_NOALLOC_SCRATCH_BYTES == atf::kNoAllocScratchBytes, "scratch size");
+
 using namespace atf;
 
 namespace {
@@ -339,6 +341,59 @@ atf_status attend_impl(const void *q, const void *k, const void *v, void *out, i
     float *part = (float *)((char *)workspace + prefill_ws_bytes(B, Hkv, Sk, d, dtype));
     return attend_core(q, k, v, out, B, Hq, Hkv, Sq, Sk, d, layout, rope_base, alpha, causal, pos0, dtype, kv,
                        (unsigned long long *)workspace, part, n_ksplit, skipped_out, s);
+}
+
+// Checks shared by the paged decode entry points (everything but the scratch).
+atf_status paged_decode_checks(const void *q, const void *kpool, const void *vpool, const void *out,
+                               const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
+                               int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d,
+                               int32_t rope_layout, double rope_base, double alpha, int32_t causal, int64_t pos0,
+                               atf_dtype dtype) {
+    atf_status st = check_shape(B, Hq, Hkv, max_len, d, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
+    if (!page_table || !seq_lens || ((uintptr_t)page_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
+        return ATF_ERR_INVALID_ARG;
+    if (max_pages < 1 || num_pages < 1 || max_len > (int64_t)max_pages * kKeyTile) return ATF_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
+    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
+    return ATF_OK;
+}
+
+// Paged decode over a checked shape with `workspace` (at least paged_ws_bytes):
+// counter, rotated queries, split partials.
+atf_status paged_decode_launch(const void *q, const void *kpool, const void *vpool, void *out,
+                               const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
+                               int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d,
+                               int32_t rope_layout, double rope_base, double alpha, int64_t pos0, void *workspace,
+                               uint64_t *skipped_out, hipStream_t s) {
+    DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = kpool;
+    a.v = vpool;
+    a.out = out;
+    a.counter = (unsigned long long *)workspace;
+    a.qrot = (unsigned *)((char *)workspace + kHeaderBytes);
+    a.part = (float *)((char *)workspace + kHeaderBytes + dec_qrot_bytes(B, Hq, d));
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.group = Hq / Hkv;
+    a.S = (int)max_len;
+    a.page_table = page_table;
+    a.seq_lens = seq_lens;
+    a.max_pages = max_pages;
+    a.num_pages = num_pages;
+    a.pos0 = pos0;
+    a.gptj = rope_layout;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    window_table_i32(d, rope_base, alpha, a.W);
+    theta_table(d, rope_base, a.theta);
+    a.n_slabs = (a.group + kDecodeHeads - 1) / kDecodeHeads;
+    paged_plan(Hq, Hkv, max_len, d, a.split_budget, a.nsplit);
+    if (launch_decode_paged_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
+    return read_counter(a.counter, skipped_out, s);
 }
 
 }  // namespace
@@ -751,44 +806,32 @@ atf_status atf_decode_paged(const void *q, const void *kpool, const void *vpool,
                             int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len, int32_t d, int32_t rope_layout,
                             double rope_base, double alpha, int32_t causal, int64_t pos0, atf_dtype dtype,
                             void *workspace, size_t workspace_bytes, uint64_t *skipped_out, atf_stream_t stream) {
-    atf_status st = check_shape(B, Hq, Hkv, max_len, d, rope_base, alpha, causal, pos0, dtype);
+    atf_status st = paged_decode_checks(q, kpool, vpool, out, page_table, seq_lens, max_pages, num_pages, B, Hq, Hkv,
+                                        max_len, d, rope_layout, rope_base, alpha, causal, pos0, dtype);
     if (st != ATF_OK) return st;
-    if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
-    if (!page_table || !seq_lens || ((uintptr_t)page_table & 3u) != 0 || ((uintptr_t)seq_lens & 3u) != 0)
-        return ATF_ERR_INVALID_ARG;
-    if (max_pages < 1 || num_pages < 1 || max_len > (int64_t)max_pages * kKeyTile) return ATF_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(kpool) || !aligned16(vpool) || !aligned16(out)) return ATF_ERR_INVALID_ARG;
-    if (dtype != ATF_BF16) return ATF_ERR_UNSUPPORTED;
     if (!aligned16(workspace) || workspace_bytes < paged_ws_bytes(B, Hq, Hkv, max_len, d))
         return ATF_ERR_WORKSPACE;
+    return paged_decode_launch(q, kpool, vpool, out, page_table, seq_lens, max_pages, num_pages, B, Hq, Hkv,
+                               max_len, d, rope_layout, rope_base, alpha, pos0, workspace, skipped_out,
+                               (hipStream_t)stream);
+}
+
+atf_status atf_decode_paged_noalloc(const void *q, const void *kpool, const void *vpool, void *out,
+                                    const int32_t *page_table, const int32_t *seq_lens, int32_t max_pages,
+                                    int32_t num_pages, int32_t B, int32_t Hq, int32_t Hkv, int64_t max_len,
+                                    int32_t d, int32_t rope_layout, double rope_base, double alpha, int32_t causal,
+                                    int64_t pos0, atf_dtype dtype, uint64_t *skipped_out, atf_stream_t stream) {
+    atf_status st = paged_decode_checks(q, kpool, vpool, out, page_table, seq_lens, max_pages, num_pages, B, Hq, Hkv,
+                                        max_len, d, rope_layout, rope_base, alpha, causal, pos0, dtype);
+    if (st != ATF_OK) return st;
+    // the shape must fit the library's scratch; checked before any HIP call
+    if (paged_ws_bytes(B, Hq, Hkv, max_len, d) > (size_t)ATF_NOALLOC_SCRATCH_BYTES) return ATF_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    DecodeArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.q = q;
-    a.k = kpool;
-    a.v = vpool;
-    a.out = out;
-    a.counter = (unsigned long long *)workspace;
-    a.qrot = (unsigned *)((char *)workspace + kHeaderBytes);
-    a.part = (float *)((char *)workspace + kHeaderBytes + dec_qrot_bytes(B, Hq, d));
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.group = Hq / Hkv;
-    a.S = (int)max_len;
-    a.page_table = page_table;
-    a.seq_lens = seq_lens;
-    a.max_pages = max_pages;
-    a.num_pages = num_pages;
-    a.pos0 = pos0;
-    a.gptj = rope_layout;
-    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
-    window_table_i32(d, rope_base, alpha, a.W);
-    theta_table(d, rope_base, a.theta);
-    a.n_slabs = (a.group + kDecodeHeads - 1) / kDecodeHeads;
-    paged_plan(Hq, Hkv, max_len, d, a.split_budget, a.nsplit);
-    if (launch_decode_paged_bf16(a, d, s) != hipSuccess) return ATF_ERR_HIP;
-    return read_counter(a.counter, skipped_out, s);
+    void *scratch = nullptr;
+    if (noalloc_scratch(s, &scratch) != hipSuccess) return ATF_ERR_HIP;
+    if (!scratch) return ATF_ERR_INVALID_ARG;  // the stream belongs to another device than the current one
+    return paged_decode_launch(q, kpool, vpool, out, page_table, seq_lens, max_pages, num_pages, B, Hq, Hkv,
+                               max_len, d, rope_layout, rope_base, alpha, pos0, scratch, skipped_out, s);
 }
 
 }  // extern "C"

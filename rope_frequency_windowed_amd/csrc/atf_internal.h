@@ -27,6 +27,8 @@ constexpr int kQueryTileF32 = 64; // queries per prefill workgroup (fp32)
 constexpr int kMaxSplits = 256;   // decode splits per (batch, kv head)
 constexpr int kDecodeHeads = 8;   // query heads one decode workgroup serves
 constexpr int kWindowInf = 0x7fffffff;
+// Library-owned device scratch of atf_decode_paged_noalloc, per GPU.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 
 // Padded key count: every tile is full, padding rows hold zeros.
 // rotated-key / transposed-value rows kept per (b, kv head): whole prefill tiles
@@ -127,5 +129,9 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s);
+// Device address of the current GPU's copy of the library's scratch array
+// (kNoAllocScratchBytes); looked up once per device and kept.  *ptr = NULL
+// when `s` (non-null) belongs to a device other than the current one.
+hipError_t noalloc_scratch(hipStream_t s, void **ptr);
 
 }  // namespace atf

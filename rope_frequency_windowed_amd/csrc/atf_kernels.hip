@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace atf {
 namespace {
@@ -2431,6 +2432,46 @@ hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) 
 hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(p);
     return hipGetLastError();
+}
+
+}  // namespace atf
+
+// Scratch of the entry point that allocates nothing (paged decode: counter,
+// rotated queries, split partials).  Every GPU the library runs on holds its
+// own copy for the life of the process; host code reaches it only through the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[atf::kNoAllocScratchBytes];
+
+namespace atf {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(hipStream_t s, void **ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (s != nullptr) {
+        int sdev = -1;
+        e = hipStreamGetDevice(s, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipSuccess;  // *ptr stays NULL: the caller reports the mismatch
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace atf

@@ -339,6 +339,47 @@ def test_paged_decode_rejects(lib, kw, expect):
     assert _call_pdecode(lib, **kw) == expect
 
 
+def _call_pdecode_noalloc(lib, **kw):
+    args = dict(q=16, kp=32, vp=48, out=64, pt=128, sl=256, max_pages=4, num_pages=8, B=2, Hq=4, Hkv=2,
+                max_len=200, d=128, layout=0, base=1e6, alpha=1.0, causal=1, pos0=0, dtype=atf.ATF_BF16,
+                skipped=None, stream=None)
+    args.update(kw)
+    return lib.atf_decode_paged_noalloc(*(ctypes.c_void_p(args[x]) for x in ("q", "kp", "vp", "out", "pt", "sl")),
+                                        args["max_pages"], args["num_pages"], args["B"], args["Hq"], args["Hkv"],
+                                        args["max_len"], args["d"], args["layout"], args["base"], args["alpha"],
+                                        args["causal"], args["pos0"], args["dtype"], args["skipped"], args["stream"])
+
+
+def _noalloc_max_batch(Hq, Hkv, max_len, d):
+    b = 1
+    while atf.atf_decode_paged_workspace_bytes(b + 1, Hq, Hkv, max_len, d) <= bnd.NOALLOC_SCRATCH_BYTES:
+        b += 1
+    return b
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), bnd.ATF_ERR_INVALID_ARG), (dict(sl=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(sl=258), bnd.ATF_ERR_INVALID_ARG), (dict(max_len=257), bnd.ATF_ERR_INVALID_ARG),
+    (dict(max_len=0), bnd.ATF_ERR_INVALID_ARG), (dict(num_pages=0), bnd.ATF_ERR_INVALID_ARG),
+    (dict(Hq=5), bnd.ATF_ERR_INVALID_ARG), (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED), (dict(alpha=float("nan")), bnd.ATF_ERR_INVALID_ARG),
+    (dict(layout=2), bnd.ATF_ERR_INVALID_ARG),
+    # beyond the library's scratch: rejected on the host, before any HIP call
+    (dict(B=18, Hq=28, Hkv=4, max_len=262144, max_pages=4096), bnd.ATF_ERR_WORKSPACE),
+    (dict(B=16, Hq=64, Hkv=1, max_len=262144, max_pages=4096, d=256), bnd.ATF_ERR_WORKSPACE),
+])
+def test_paged_decode_noalloc_rejects(lib, kw, expect):
+    assert _call_pdecode_noalloc(lib, **kw) == expect
+
+
+def test_noalloc_scratch_limit():
+    """The stated limit: at Hq=28, Hkv=4, d=128 the library's 32 MiB scratch
+    holds a batch of 17 sequences and no more."""
+    assert _noalloc_max_batch(28, 4, 262144, 128) == 17
+    assert atf.atf_decode_paged_workspace_bytes(17, 28, 4, 262144, 128) <= 32 << 20
+    assert atf.atf_decode_paged_workspace_bytes(18, 28, 4, 262144, 128) > 32 << 20
+
+
 def test_probe_library_exports_and_checks_arguments():
     """The microbenchmark library exports what include/atf_probes.h declares
     and rejects bad arguments on the host (nothing is launched)."""
