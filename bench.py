@@ -128,11 +128,53 @@ def cpu_baseline(q, k, v, cfg, seconds_hint=12.0):
         "unit": "tok/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "host_cores": len(os.sched_getaffinity(0)),
         "sample": ("%d query rows (%d per head, seeded, incl. first and last) of the S=%d layer: "
                    "%.3g key visits in %.2f s incl. rotating the 4 key heads; tok/s extrapolated "
                    "linearly in key visits to the full layer (%.3g visits)"
                    % (len(rows), per_head, S, visits, dt, total_visits)),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_decode_full(q, k, v, cfg):
+    """The oracle over the whole decode workload (every query row of the batch
+    against all its keys), timed on the host: no sampling, no extrapolation."""
+    import oracle
+    qq, kk, vv = (t.detach().to("cpu").float().contiguous().numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    _, skipped = oracle.attention(qq, kk, vv, base=cfg["base"], alpha=cfg["alpha"], q_pos0=cfg["S"], k_pos0=0)
+    dt = time.perf_counter() - t0
+    return {"value": cfg["B"] / dt, "unit": "tok/s (decode step)", "seconds": dt, "cores": oracle.num_threads(),
+            "kind": "oracle", "dropped_terms": skipped,
+            "sample": "all %d query rows (B=%d x Hq=%d) over %d keys each, in full"
+                      % (cfg["B"] * cfg["Hq"], cfg["B"], cfg["Hq"], cfg["S"])}
+
+
+def cpu_small_full():
+    """The oracle over the small fp32 prefill (B=1, H=1, S=256, d=64, base 1e4,
+    alpha 1) in full: wall time and the exact dropped-term count."""
+    import oracle
+    import torch
+    from rope_frequency_windowed_amd.inputs import make_qkv
+    q, k, v = make_qkv(1, 1, 1, 256, 256, 64, dtype=torch.float32)
+    qq, kk, vv = (t.numpy() for t in (q, k, v))
+    t0 = time.perf_counter()
+    _, skipped = oracle.attention(qq, kk, vv, base=1e4, alpha=1.0)
+    dt = time.perf_counter() - t0
+    return {"value": 256 / dt, "unit": "tok/s", "seconds": dt, "cores": oracle.num_threads(), "kind": "oracle",
+            "dropped_terms": skipped, "sample": "S=256, d=64, one head, fp32, in full"}
 
 
 def copy_probe():
@@ -416,6 +458,9 @@ def main():
         kcache = torch.empty(atf.atf_decode_kcache_bytes(D["B"], D["Hkv"], D["S"], D["d"]),
                              dtype=torch.uint8, device=dev)
         atf.atf_decode_pack_k(kk, kcache, k_begin=0, cap=D["S"], rope_base=D["base"])
+        # a serving step appends the token the previous step produced (the last
+        # one, rewritten with the same bytes) and then decodes over all S keys
+        kk_new, kv_new = kk[:, :, -1:].contiguous(), kv[:, :, -1:].contiguous()
         del kk
     if do_paged:
         import numpy as np
@@ -430,6 +475,7 @@ def main():
         kpool = torch.empty(n_pages, D["Hkv"], page_b // D["Hkv"], dtype=torch.uint8, device=dev)
         vpool = torch.empty_like(kpool)
         atf.atf_paged_write(pk, pv, kpool, vpool, ptab, k_begin=0, rope_base=D["base"])
+        pk_new, pv_new = pk[:, :, -1:].contiguous(), pv[:, :, -1:].contiguous()
         del pk, pv
         plens = torch.full((D["B"],), D["S"], dtype=torch.int32, device=dev)
         pws = torch.empty(atf.atf_decode_paged_workspace_bytes(D["B"], D["Hq"], D["Hkv"], D["S"], D["d"]),
@@ -480,12 +526,35 @@ def main():
                                  alpha=DECODE["alpha"], ws=pws)
             if ev is not None:
                 ev[8].record(stream)
+        if do_kcache:  # serving step: append the newest token, then decode
+            cold()
+            if ev is not None:
+                ev[9].record(stream)
+            atf.atf_decode_append_kv(kk_new, kv_new, kcache, kv, k_begin=DECODE["S"] - 1, cap=DECODE["S"],
+                                     rope_base=DECODE["base"])
+            if ev is not None:
+                ev[10].record(stream)
+            atf.atf_decode_kcache(kq, kcache, kv, kout, S=DECODE["S"], rope_base=DECODE["base"],
+                                  alpha=DECODE["alpha"], ws=kws)
+            if ev is not None:
+                ev[11].record(stream)
+        if do_paged:
+            cold()
+            if ev is not None:
+                ev[12].record(stream)
+            atf.atf_paged_write(pk_new, pv_new, kpool, vpool, ptab, k_begin=DECODE["S"] - 1, rope_base=DECODE["base"])
+            if ev is not None:
+                ev[13].record(stream)
+            atf.atf_decode_paged(pq, kpool, vpool, ptab, plens, pout, max_len=DECODE["S"], rope_base=DECODE["base"],
+                                 alpha=DECODE["alpha"], ws=pws)
+            if ev is not None:
+                ev[14].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(15)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -525,6 +594,15 @@ def main():
                                              "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                              "algorithmic_bytes_per_launch": nbytes,
                                              "traffic": read_traffic(DECODE_COUNTERS_FILE)})}
+        # every memory read is a whole 128-byte line and each half of a d=128
+        # bf16 key row is one line holding the slowest pair, so this layout
+        # reads every key byte: its algorithmic rate is capped at
+        # algorithmic / dense bytes of the attainable HBM rate
+        dense = decode_algorithmic_bytes(atf, **dict(DECODE, alpha=math.inf))
+        res["decode"]["structural_cap"] = {
+            "dense_bytes_per_launch": dense, "algorithmic_over_dense": nbytes / dense,
+            "cap_frac_of_peak": nbytes / dense * attainable["hbm_read_gbs"] / HBM_PEAK_GBS,
+            "note": "standard [S][d] cache, half-split pairs: 128-byte lines hold both kept and dropped pairs"}
         config["decode"] = dict(DECODE)
         log("decode: %.3f ms, %.3g algorithmic bytes, %.0f GB/s (%.1f%% of HBM peak)"
             % (dec_ms, nbytes, gbs, 100 * gbs / HBM_PEAK_GBS))
@@ -558,6 +636,28 @@ def main():
                                 "traffic": read_traffic(PAGED_COUNTERS_FILE)})}
         log("decode (paged key cache): %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
             % (pg_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+    for name, on, e0, e1, e2, how in (
+            ("decode_kcache_step", do_kcache, 9, 10, 11,
+             "atf_decode_append_kv of the newest token (n=1, key rotated into the planes, value row), then "
+             "atf_decode_kcache over all S keys"),
+            ("decode_paged_step", do_paged, 12, 13, 14,
+             "atf_paged_write of the newest token of every sequence (n=1), then atf_decode_paged")):
+        if not on:
+            continue
+        app_ms = sum(e[e0].elapsed_time(e[e1]) for e in events) / args.steps
+        dec_ms = sum(e[e1].elapsed_time(e[e2]) for e in events) / args.steps
+        st_ms, st_med, st_min = leg_stats([e[e0].elapsed_time(e[e2]) for e in events])
+        D = DECODE
+        append_bytes = 2 * 2 * D["B"] * D["Hkv"] * D["d"] * 2   # read k, v of one token; write both
+        nbytes = decode_algorithmic_bytes(atf, **D) + append_bytes
+        gbs = nbytes / (st_ms * 1e-3) / 1e9
+        res[name] = {
+            "value": gbs, "unit": "GB/s", "ms": st_ms, "ms_median": st_med, "ms_min": st_min,
+            "append_ms": app_ms, "decode_ms": dec_ms, "tok_per_s": D["B"] / (st_ms * 1e-3), "step": how,
+            "roofline": attain({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes})}
+        log("%s: append %.4f ms + decode %.3f ms = %.3f ms, %.0f GB/s (%.1f%% of HBM peak)"
+            % (name, app_ms, dec_ms, st_ms, gbs, 100 * gbs / HBM_PEAK_GBS))
         if args.only == "paged":
             res["value"], res["unit"] = gbs, "GB/s"
     if do_variants:
@@ -571,6 +671,9 @@ def main():
     res["config"] = config
     if do_prefill and not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(q, k, v, PREFILL)
+        if do_decode:
+            res["cpu_baseline"]["decode_full"] = cpu_decode_full(dq, dk, dv, DECODE)
+        res["cpu_baseline"]["small_fp32_full"] = cpu_small_full()
         log("cpu baseline:", res["cpu_baseline"])
     print(json.dumps(res))
 

@@ -286,7 +286,7 @@ atf_status atf_decode(const void *q, const void *k, const void *v, void *out,
  */
 
 /* Bytes of a key cache of capacity cap keys (0 if cap is not a positive
- * multiple of 64 below 2^31 or d is not 64 or 128). */
+ * multiple of 64 below 2^31 or d is not 64, 128 or 256). */
 size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d);
 
 /*
@@ -300,6 +300,25 @@ size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d);
 atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n,
                              int64_t k_begin, int64_t cap, int32_t d, int32_t rope_layout, double rope_base,
                              int64_t pos0, atf_dtype dtype, atf_stream_t stream);
+
+/*
+ * The cache write of one serving decode step over this layout (source page
+ * "ATFlash: RoPE-Frequenzen kuerzen Attention-Arbeit um bis zu 57 Prozent",
+ * section "Die Zahlen - und ihre Grenze": the method lives in the serving
+ * decode kernel, so each step's new key enters the cache it reads): keys k and
+ * values v, both [B][Hkv][n][d] (pre-RoPE keys, bf16), become cache entries
+ * k_begin .. k_begin + n - 1 -- keys rotated into kcache as atf_decode_pack_k
+ * writes them, values copied as rows of vcache [B][Hkv][cap][d] (the value
+ * layout atf_decode_kcache reads) -- in one launch.  A step appends the
+ * token the previous step produced (n = 1, k_begin = the current length) and
+ * then decodes with atf_decode_kcache.  Same requirements and errors as
+ * atf_decode_pack_k; v and vcache must both be NULL (keys only, the same as
+ * atf_decode_pack_k) or both non-NULL and 16-byte aligned, else
+ * ATF_ERR_INVALID_ARG.  Asynchronous on `stream`.
+ */
+atf_status atf_decode_append_kv(const void *k, const void *v, void *kcache, void *vcache, int32_t B, int32_t Hkv,
+                                int64_t n, int64_t k_begin, int64_t cap, int32_t d, int32_t rope_layout,
+                                double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream);
 
 /*
  * atf_decode over that cache: query q [B][Hq][1][d] at position pos0 + S over

@@ -12,7 +12,7 @@ function names.
 """
 from ._binding import (  # noqa: F401
     ALPHA_INF, ATF_BF16, ATF_F32, EXPORTED, LIB_PATH, W_INF, AtfError, atf_decode, atf_decode_kcache,
-    atf_decode_kcache_bytes, atf_decode_pack_k, atf_decode_paged, atf_decode_paged_noalloc,
+    atf_decode_kcache_bytes, atf_decode_pack_k, atf_decode_append_kv, atf_decode_paged, atf_decode_paged_noalloc,
     atf_decode_paged_workspace_bytes, NOALLOC_SCRATCH_BYTES,
     atf_decode_workspace_bytes, atf_paged_page_bytes,
     atf_paged_write, atf_prefill, atf_prefill_attend, atf_prefill_chunk, atf_prefill_chunk_workspace_bytes,

@@ -30,7 +30,7 @@ EXPORTED = (
     "atf_prefill_chunk_cached", "atf_decode_workspace_bytes", "atf_decode",
     "atf_decode_kcache_bytes", "atf_decode_pack_k", "atf_decode_kcache",
     "atf_paged_page_bytes", "atf_decode_paged_workspace_bytes", "atf_paged_write", "atf_decode_paged",
-    "atf_decode_paged_noalloc",
+    "atf_decode_paged_noalloc", "atf_decode_append_kv",
 )
 NOALLOC_SCRATCH_BYTES = 32 << 20  # ATF_NOALLOC_SCRATCH_BYTES
 
@@ -97,6 +97,9 @@ def _lib():
     lib.atf_decode_kcache_bytes.restype = sz
     lib.atf_decode_pack_k.argtypes = [vp, vp, i32, i32, i64, i64, i64, i32, i32, f64, i64, ctypes.c_int, vp]
     lib.atf_decode_pack_k.restype = ctypes.c_int
+    lib.atf_decode_append_kv.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i64, i32, i32, f64, i64, ctypes.c_int,
+                                         vp]
+    lib.atf_decode_append_kv.restype = ctypes.c_int
     lib.atf_decode_kcache.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, i64, i32, i32, f64, f64, i32, i64,
                                       ctypes.c_int, vp, sz, u64p, vp]
     lib.atf_decode_kcache.restype = ctypes.c_int
@@ -371,6 +374,17 @@ def atf_decode_pack_k(k, kcache, *, k_begin: int, cap: int, rope_base: float, po
     _check(_lib().atf_decode_pack_k(_dev(k, "k"), _dev(kcache, "kcache"), B, Hkv, n, int(k_begin), int(cap), d,
                                     _layout_code(rope_layout), float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
            "atf_decode_pack_k")
+
+
+def atf_decode_append_kv(k, v, kcache, vcache, *, k_begin: int, cap: int, rope_base: float, pos0: int = 0,
+                         rope_layout="neox"):
+    """Write k, v [B,Hkv,n,d] (pre-RoPE, bf16) as entries k_begin.. of the key
+    cache kcache and the value cache vcache [B,Hkv,cap,d] in one launch."""
+    B, Hkv, n, d = k.shape
+    _check(_lib().atf_decode_append_kv(_dev(k, "k"), _dev(v, "v"), _dev(kcache, "kcache"), _dev(vcache, "vcache"),
+                                       B, Hkv, n, int(k_begin), int(cap), d, _layout_code(rope_layout),
+                                       float(rope_base), int(pos0), _dtype_code(k), _stream(k.device)),
+           "atf_decode_append_kv")
 
 
 def atf_decode_kcache(q, kcache, v, out=None, *, S: int, rope_base: float, alpha: float, causal: int = 1,

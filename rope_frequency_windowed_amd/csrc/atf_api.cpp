@@ -687,6 +687,15 @@ size_t atf_decode_kcache_bytes(int32_t B, int32_t Hkv, int64_t cap, int32_t d) {
 atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv, int64_t n, int64_t k_begin,
                              int64_t cap, int32_t d, int32_t rope_layout, double rope_base, int64_t pos0,
                              atf_dtype dtype, atf_stream_t stream) {
+    return atf_decode_append_kv(k, nullptr, kcache, nullptr, B, Hkv, n, k_begin, cap, d, rope_layout, rope_base, pos0,
+                                dtype, stream);
+}
+
+atf_status atf_decode_append_kv(const void *k, const void *v, void *kcache, void *vcache, int32_t B, int32_t Hkv,
+                                int64_t n, int64_t k_begin, int64_t cap, int32_t d, int32_t rope_layout,
+                                double rope_base, int64_t pos0, atf_dtype dtype, atf_stream_t stream) {
+    if ((v == nullptr) != (vcache == nullptr)) return ATF_ERR_INVALID_ARG;
+    if (v && (!aligned16(v) || !aligned16(vcache))) return ATF_ERR_INVALID_ARG;
     if (bad_layout(rope_layout)) return ATF_ERR_INVALID_ARG;
     if (!k || !kcache || !aligned16(k) || !aligned16(kcache)) return ATF_ERR_INVALID_ARG;
     if (B < 1 || Hkv < 1 || n < 1 || k_begin < 0) return ATF_ERR_INVALID_ARG;
@@ -701,6 +710,8 @@ atf_status atf_decode_pack_k(const void *k, void *kcache, int32_t B, int32_t Hkv
     std::memset(&a, 0, sizeof(a));
     a.k = k;
     a.kc = kcache;
+    a.v = v;
+    a.vc = vcache;
     a.B = B;
     a.Hkv = Hkv;
     a.n = (int)n;

@@ -102,6 +102,8 @@ struct DecodeArgs {
 struct KPackArgs {
     const void *k;                    // [B][Hkv][n][d] pre-RoPE keys
     void *kc;                         // the key cache, capacity cap keys per (b, kv head)
+    const void *v;                    // nullable: [B][Hkv][n][d] values, copied as rows k_begin.. of vc
+    void *vc;                         // the value cache [B][Hkv][cap][d] (with v)
     int B, Hkv, n, cap;
     long long k_begin, pos0;          // key k[.., i, :] is cache key k_begin + i at pos0 + k_begin + i
     int gptj;                         // rotary pairs of k: 0 = (p, p + d/2), 1 = (2p, 2p + 1)

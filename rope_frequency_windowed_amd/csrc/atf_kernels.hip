@@ -1817,13 +1817,21 @@ __device__ inline long long dec_prefix_bytes(int j, int S, const WaveWin<D / 2> 
 
 template <int D>
 __global__ __launch_bounds__(256) void kpack_bf16_kernel(KPackArgs a) {
-    constexpr int P = D / 2, NPL = P / 4;
+    constexpr int P = D / 2, NPL = P / 4, CHV = D / 8;
     constexpr unsigned KPBLK = NPL * 1024;
     const int bk = blockIdx.y;
-    const long long total = (long long)a.n * NPL;
+    // per token: NPL key planes, then (with values) CHV 16-byte value chunks
+    const int U = a.v ? NPL + CHV : NPL;
+    const long long total = (long long)a.n * U;
     for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
-        const int i = (int)(e / NPL), pg = (int)(e % NPL);
+        const int i = (int)(e / U), pg = (int)(e % U);
         const long long j = a.k_begin + i;
+        if (pg >= NPL) {  // value row j, chunk pg - NPL
+            const int c = pg - NPL;
+            const u32x4 val = *(const u32x4 *)((const unsigned short *)a.v + ((long long)bk * a.n + i) * D + c * 8);
+            *(u32x4 *)((unsigned short *)a.vc + ((long long)bk * a.cap + j) * D + c * 8) = val;
+            continue;
+        }
         const unsigned short *src = (const unsigned short *)a.k + ((long long)bk * a.n + i) * D;
         u32x2 lo, hi;
         load_pair_pieces(src, 4 * pg, P, a.gptj != 0, lo, hi);
@@ -2380,7 +2388,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s) {
 }
 
 hipError_t launch_kpack_bf16(const KPackArgs &a, int d, hipStream_t s) {
-    const long long total = (long long)a.n * (d / 8);
+    const long long total = (long long)a.n * (a.v ? d / 8 + d / 8 : d / 8);
     const unsigned gx = (unsigned)std::min<long long>((total + 255) / 256, 65535);
     dim3 grid(gx, (unsigned)(a.B * a.Hkv));
     if (d == 256) kpack_bf16_kernel<256><<<grid, 256, 0, s>>>(a);

@@ -257,6 +257,28 @@ def test_pack_rejects(lib, kw, expect):
     assert _call_pack(lib, **kw) == expect
 
 
+def _call_append_kv(lib, **kw):
+    args = dict(k=16, v=4096, kc=32, vc=8192, B=1, Hkv=2, n=10, k_begin=0, cap=128, d=128, layout=0, base=1e6,
+                pos0=0, dtype=atf.ATF_BF16, stream=None)
+    args.update(kw)
+    return lib.atf_decode_append_kv(*(ctypes.c_void_p(args[x]) for x in ("k", "v", "kc", "vc")), args["B"],
+                                    args["Hkv"], args["n"], args["k_begin"], args["cap"], args["d"], args["layout"],
+                                    args["base"], args["pos0"], args["dtype"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=None), bnd.ATF_ERR_INVALID_ARG), (dict(kc=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(v=None), bnd.ATF_ERR_INVALID_ARG), (dict(vc=None), bnd.ATF_ERR_INVALID_ARG),
+    (dict(v=4100), bnd.ATF_ERR_INVALID_ARG), (dict(vc=8200), bnd.ATF_ERR_INVALID_ARG),
+    (dict(n=0), bnd.ATF_ERR_INVALID_ARG), (dict(k_begin=120, n=10), bnd.ATF_ERR_INVALID_ARG),
+    (dict(cap=100), bnd.ATF_ERR_INVALID_ARG), (dict(d=96), bnd.ATF_ERR_UNSUPPORTED),
+    (dict(dtype=atf.ATF_F32), bnd.ATF_ERR_UNSUPPORTED), (dict(layout=3), bnd.ATF_ERR_INVALID_ARG),
+    (dict(pos0=-1), bnd.ATF_ERR_INVALID_ARG), (dict(base=0.5), bnd.ATF_ERR_INVALID_ARG),
+])
+def test_append_kv_rejects(lib, kw, expect):
+    assert _call_append_kv(lib, **kw) == expect
+
+
 def _call_kcache(lib, **kw):
     args = dict(q=16, kc=32, v=48, out=64, B=1, Hq=4, Hkv=2, S=128, cap=128, d=128, layout=0, base=1e6, alpha=1.0,
                 causal=1, pos0=0, dtype=atf.ATF_BF16, ws=4096, ws_bytes=1, skipped=None, stream=None)

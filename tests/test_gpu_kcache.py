@@ -160,3 +160,42 @@ def test_kcache_workload_full(env):
     dense, _ = oracle.attention(q, k, v, base=1e6, alpha=math.inf, q_pos0=262144, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, dense, "kcache 256K")
     assert skipped == ref_skipped
+
+
+STEP = [
+    # B, Hq, Hkv, S, cap, d, base, alpha
+    (8, 28, 4, 20000, 20032, 128, 1e6, 1.0),
+    (2, 7, 1, 4097, 4160, 128, 1e6, 2.0),
+    (1, 4, 2, 1, 64, 64, 1e4, 1.0),
+    (1, 8, 2, 3001, 3008, 256, 1e6, 1.0),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,cap,d,base,alpha", STEP)
+def test_kcache_step_append_then_decode(env, B, Hq, Hkv, S, cap, d, base, alpha):
+    """One serving step: the caches hold S - 1 tokens, the step appends token
+    S - 1 (its key rotated into the planes, its value row) with one
+    atf_decode_append_kv call of n = 1, then decodes the query at S over S
+    keys.  Checked against the oracle, and bit for bit against the decode over
+    caches written in one go."""
+    torch, oracle, atf, inputs = env
+    log("case: kcache append-then-decode %s" % ((B, Hq, Hkv, S, cap, d, base, alpha),))
+    dev = torch.device("cuda:0")
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, 1, S, d, dtype=torch.bfloat16, device=dev)
+    kc = torch.empty(atf.atf_decode_kcache_bytes(B, Hkv, cap, d), dtype=torch.uint8, device=dev)
+    vc = torch.zeros(B, Hkv, cap, d, dtype=torch.bfloat16, device=dev)
+    if S > 1:
+        atf.atf_decode_append_kv(k[:, :, :S - 1].contiguous(), v[:, :, :S - 1].contiguous(), kc, vc, k_begin=0,
+                                 cap=cap, rope_base=base)
+    atf.atf_decode_append_kv(k[:, :, S - 1:].contiguous(), v[:, :, S - 1:].contiguous(), kc, vc, k_begin=S - 1,
+                             cap=cap, rope_base=base)
+    out, skipped = atf.atf_decode_kcache(q, kc, vc, S=S, rope_base=base, alpha=alpha, return_skipped=True)
+    kc1, vc1 = make_cache(env, k, v, cap, base)
+    out1 = atf.atf_decode_kcache(q, kc1, vc1, S=S, rope_base=base, alpha=alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(vc[:, :, :S], v), "appended value rows"
+    assert torch.equal(out, out1), "append-then-decode differs from the decode over a cache written in one go"
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=S, k_pos0=0)
+    dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, q_pos0=S, k_pos0=0)
+    check_bf16(out.float().cpu().numpy(), ref, dense, "kcache step %s" % ((B, Hq, Hkv, S, d),))
+    assert skipped == ref_skipped == B * Hq * atf.atf_skipped_pair_products(S, d, base, alpha, 1, 1)

@@ -163,3 +163,39 @@ def test_paged_workload_ragged(env):
     torch.cuda.synchronize()
     ref_skipped = check_against_oracle(env, q, k, v, out, lens, 1e6, 1.0, label="paged 256K ragged")
     assert skipped == ref_skipped
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,d,base,alpha", [
+    (8, 28, 4, 20000, 128, 1e6, 1.0),
+    (3, 7, 1, 4097, 128, 1e6, 2.0),
+    (2, 4, 2, 1, 64, 1e4, 1.0),
+])
+def test_paged_step_append_then_decode(env, B, Hq, Hkv, S, d, base, alpha):
+    """One serving step over pages: every sequence holds S - 1 tokens, the step
+    writes token S - 1 of each (atf_paged_write, n = 1), then decodes the
+    queries at S.  Checked against the oracle and bit for bit against the same
+    decode over pages written in one go."""
+    torch, oracle, atf, inputs = env
+    log("case: paged append-then-decode %s" % ((B, Hq, Hkv, S, d, base, alpha),))
+    dev = torch.device("cuda:0")
+    max_pages = (S + 63) // 64
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, 1, S, d, dtype=torch.bfloat16, device=dev)
+    num_pages = B * max_pages + 2
+    perm = np.random.default_rng(3).permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    pt = torch.as_tensor(perm.astype(np.int32), device=dev)
+    pb = atf.atf_paged_page_bytes(Hkv, d)
+    pools = [torch.zeros(num_pages, Hkv, pb // Hkv, dtype=torch.uint8, device=dev) for _ in range(4)]
+    if S > 1:
+        atf.atf_paged_write(k[:, :, :S - 1].contiguous(), v[:, :, :S - 1].contiguous(), pools[0], pools[1], pt,
+                            k_begin=0, rope_base=base)
+    atf.atf_paged_write(k[:, :, S - 1:].contiguous(), v[:, :, S - 1:].contiguous(), pools[0], pools[1], pt,
+                        k_begin=S - 1, rope_base=base)
+    atf.atf_paged_write(k, v, pools[2], pools[3], pt, k_begin=0, rope_base=base)
+    sl = torch.full((B,), S, dtype=torch.int32, device=dev)
+    out, skipped = atf.atf_decode_paged(q, pools[0], pools[1], pt, sl, max_len=S, rope_base=base, alpha=alpha,
+                                        return_skipped=True)
+    out1 = atf.atf_decode_paged(q, pools[2], pools[3], pt, sl, max_len=S, rope_base=base, alpha=alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out1), "append-then-decode differs from the decode over pages written in one go"
+    ref_skipped = check_against_oracle(env, q, k, v, out, [S] * B, base, alpha, label="paged step")
+    assert skipped == ref_skipped == B * Hq * atf.atf_skipped_pair_products(S, d, base, alpha, 1, 1)
