@@ -183,10 +183,15 @@ def test_d256_prefill_sampled_long(env):
     out, skipped = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=1.0, return_skipped=True)
     torch.cuda.synchronize()
     assert skipped == B * Hq * atf.atf_skipped_pair_products(S, d, 1e6, 1.0, 1, 0)
-    rows = np.array([(0, h, int(i)) for h in range(Hq) for i in sample_rows(S, 3, seed=h)], dtype=np.int64)
+    from rope_frequency_windowed_amd.inputs import tile_edge_rows
+    # seeded rows plus the edges of 128-query tiles (this kernel's query tile)
+    rows = np.array([(0, h, int(i)) for h in range(Hq)
+                     for i in sorted(set(sample_rows(S, 3, seed=h)) | set(tile_edge_rows(S, 1, seed=h, tile=128)))],
+                    dtype=np.int64)
     sel = torch.as_tensor(rows, device=q.device)
     qrows = q[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
     got = out[sel[:, 0], sel[:, 1], sel[:, 2]].float().cpu().numpy()
     kk, vv = k.float().cpu().numpy(), v.float().cpu().numpy()
     ref, _ = oracle.attention(qrows, kk, vv, base=1e6, alpha=1.0, rows=rows, q_shape=(B, Hq, S, d))
-    check_bf16(got, ref, None, "d256 16K")
+    dense, _ = oracle.attention(qrows, kk, vv, base=1e6, alpha=math.inf, rows=rows, q_shape=(B, Hq, S, d))
+    check_bf16(got, ref, dense, "d256 16K")

@@ -68,9 +68,11 @@ def test_gptj_prefill_equals_neox_on_moved_dims(env):
 
 
 def test_gptj_prefill_high_frequency_heavy(env):
+    """Fast pairs scaled x1.5 where the interleaved layout stores them
+    (pairs p < d/4 = dims 0 .. d/2 - 1)."""
     torch, oracle, atf, inputs = env
     q, k, v = inputs.make_qkv(1, 4, 1, 900, 900, 128, dtype=torch.bfloat16, device=torch.device("cuda:0"),
-                              high_freq_scale=1.5)
+                              high_freq_scale=1.5, layout="gptj")
     out = atf.atf_prefill(q, k, v, rope_base=1e6, alpha=0.5, rope_layout="gptj")
     torch.cuda.synchronize()
     ref, _ = oracle.attention(q, k, v, base=1e6, alpha=0.5, layout="gptj")
