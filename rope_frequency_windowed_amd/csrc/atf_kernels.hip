@@ -324,7 +324,7 @@ __device__ inline u32x4 raw_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
 // 16 key dims of step s.
 template <int NSTEP, int S0>
 __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, unsigned ky,
-                                    const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b) {
+                                    const bf16x8_t *qf, int zero_below, s16x4_t ones_a, s16x4_t negm_b) {
     u32x4 kw = *(const u32x4 *)(lds + kbase + ((32u * S0) ^ ky));
     // words (pairs) of the first step below p_full are dropped or boundary
     kw.x = (0 < zero_below) ? 0u : kw.x;
@@ -333,9 +333,10 @@ __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, un
     kw.w = (3 < zero_below) ? 0u : kw.w;
     const f32x16_t zero16 = {};
     // -m_ref of each query column in every element: one rank-1 product (a column
-    // of ones times the row of -m_ref), so the scores leave the chain already
-    // shifted by the softmax reference
-    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, negm_b, zero16, 0, 0, 0);
+    // of ones times the row of -m_ref, on the K = 8 MFMA whose operands take
+    // two registers each), so the scores leave the chain already shifted by
+    // the softmax reference
+    f32x16_t acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones_a, negm_b, zero16, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kw), qf[S0], acc, 0, 0, 0);
 #pragma unroll
     for (int s = S0 + 1; s < NSTEP; ++s) {
@@ -347,7 +348,7 @@ __device__ inline f32x16_t qk_chain(const unsigned char *lds, unsigned kbase, un
 
 template <int NSTEP>
 __device__ inline f32x16_t qk_main(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
-                                   const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b) {
+                                   const bf16x8_t *qf, int zero_below, s16x4_t ones_a, s16x4_t negm_b) {
 #define ATF_CHAIN(s0_) qk_chain<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b)
     // s_first < NSTEP (the slowest pair is never cut); the last step is also
     // the fall-through
@@ -410,8 +411,8 @@ __device__ __attribute__((always_inline)) inline void block_pv(f32x16_t (&o)[NDB
 // one straight-line sequence so the exponentials issue between the MFMAs.
 template <int NSTEP, int S0>
 __device__ __attribute__((always_inline)) inline f32x16_t qk_chain_probs(
-    const unsigned char *lds, unsigned kbase, unsigned ky, const bf16x8_t *qf, int zero_below, bf16x8_t ones_a,
-    bf16x8_t negm_b, const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
+    const unsigned char *lds, unsigned kbase, unsigned ky, const bf16x8_t *qf, int zero_below, s16x4_t ones_a,
+    s16x4_t negm_b, const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
     const f32x16_t acc = qk_chain<NSTEP, S0>(lds, kbase, ky, qf, zero_below, ones_a, negm_b);
     block_probs(sp, pw, lsum);
     return acc;
@@ -419,7 +420,7 @@ __device__ __attribute__((always_inline)) inline f32x16_t qk_chain_probs(
 
 template <int NSTEP>
 __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, unsigned kbase, unsigned ky,
-                                         const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b,
+                                         const bf16x8_t *qf, int zero_below, s16x4_t ones_a, s16x4_t negm_b,
                                          const f32x16_t &sp, unsigned (&pw)[8], float &lsum) {
 #define ATF_CHAIN(s0_) qk_chain_probs<NSTEP, s0_>(lds, kbase, ky, qf, zero_below, ones_a, negm_b, sp, pw, lsum)
     // s_first < NSTEP (the slowest pair is never cut); the last step is also
@@ -441,7 +442,7 @@ __device__ inline f32x16_t qk_main_probs(int s_first, const unsigned char *lds, 
 template <int NSTEP, int S0>
 __device__ __attribute__((always_inline)) inline void qk_pair_chain(
     const unsigned char *lds, unsigned kb0, unsigned kb1, unsigned ky, const bf16x8_t *qf, int zero_below,
-    bf16x8_t ones_a, bf16x8_t negm_b, f32x16_t &s0, f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
+    s16x4_t ones_a, s16x4_t negm_b, f32x16_t &s0, f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
     s0 = qk_chain<NSTEP, S0>(lds, kb0, ky, qf, zero_below, ones_a, negm_b);
     block_probs(s0, pw, lsum);
     s1 = qk_chain<NSTEP, S0>(lds, kb1, ky, qf, zero_below, ones_a, negm_b);
@@ -449,7 +450,7 @@ __device__ __attribute__((always_inline)) inline void qk_pair_chain(
 
 template <int NSTEP>
 __device__ inline void qk_pair(int s_first, const unsigned char *lds, unsigned kb0, unsigned kb1, unsigned ky,
-                               const bf16x8_t *qf, int zero_below, bf16x8_t ones_a, bf16x8_t negm_b, f32x16_t &s0,
+                               const bf16x8_t *qf, int zero_below, s16x4_t ones_a, s16x4_t negm_b, f32x16_t &s0,
                                f32x16_t &s1, unsigned (&pw)[8], float &lsum) {
 #define ATF_PAIR(s0_) \
     qk_pair_chain<NSTEP, s0_>(lds, kb0, kb1, ky, qf, zero_below, ones_a, negm_b, s0, s1, pw, lsum)
@@ -618,8 +619,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     bool first = true;
     // rank-1 operands of the reference: element k = 0 of lanes 0..31 (A: ones
     // for every key row; B: -m_ref of the lane's query column), zeros elsewhere
-    const bf16x8_t ones_a = __builtin_bit_cast(bf16x8_t, (u32x4){half ? 0u : 0x3f80u, 0u, 0u, 0u});
-    bf16x8_t negm_b = __builtin_bit_cast(bf16x8_t, (u32x4){0u, 0u, 0u, 0u});
+    const s16x4_t ones_a = __builtin_bit_cast(s16x4_t, (u32x2){half ? 0u : 0x3f80u, 0u});
+    s16x4_t negm_b = __builtin_bit_cast(s16x4_t, (u32x2){0u, 0u});
     // dropped-term count: per lane where it differs between lanes, uniform
     // (whole-block) contributions in skipped_u
     unsigned long long skipped = 0, skipped_u = 0;
@@ -675,8 +676,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             if (later) {                                                                          \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[(sl) ^ 1][r] -= shift;        \
             }                                                                                     \
-            negm_b = __builtin_bit_cast(bf16x8_t,                                                 \
-                                        (u32x4){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u, 0u, 0u}); \
+            negm_b = __builtin_bit_cast(s16x4_t, (u32x2){half ? 0u : (pack_bf(-m_ref, 0.f) & 0xffffu), 0u}); \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[sl][r] -= shift;                  \
             block_probs(sacc[sl], pw[sl], lsum[sl]);                                              \
         }                                                                                         \
