@@ -1056,27 +1056,26 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
             const unsigned sw = sb ? ksw1 : ksw0;
             return *(const u32x4 *)(lt + row * (CH * 16) + (((unsigned)(4 * s + g) ^ sw) << 4));
         };
-        // query operand of step s0 with the lane's pairs below the cut zeroed
-        auto qmask = [&](int s0, int zb) -> bf16x8_t {
-            bf16x8_t qv = qf[0];
-#pragma unroll
-            for (int ss = 1; ss < NSTEP; ++ss) qv = (s0 == ss) ? qf[ss] : qv;
-            u32x4 w = __builtin_bit_cast(u32x4, qv);
+        // query operand of step s (an index known at compile time, so the
+        // fragments stay in registers) with the lane's pairs below the cut zeroed
+        auto qmask = [&](int s, int zb) -> bf16x8_t {
+            u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
             w.x = (0 < zb) ? 0u : w.x;
             w.y = (1 < zb) ? 0u : w.y;
             w.z = (2 < zb) ? 0u : w.z;
             w.w = (3 < zb) ? 0u : w.w;
             return __builtin_bit_cast(bf16x8_t, w);
         };
-        // scores of block kb over steps s0..NSTEP-1 (step s0 with the masked query qz)
-        auto scores = [&](int kb, int s0, bf16x8_t qz, f32x4_t &c0, f32x4_t &c1) {
+        // scores of block kb over steps s0..NSTEP-1 (s0 known at compile time;
+        // step s0 with the query masked below the cut, zb)
+        auto scores = [&](int kb, int s0, int zb, f32x4_t &c0, f32x4_t &c1) {
             c0 = negm;
             c1 = negm;
 #pragma unroll
             for (int s = 0; s < NSTEP; ++s) {
                 if (s < s0) continue;
                 const u32x4 k0 = kfrag(kb, 0, s), k1 = kfrag(kb, 1, s);
-                const bf16x8_t qs = (s == s0) ? qz : qf[s];
+                const bf16x8_t qs = (s == s0) ? qmask(s, zb) : qf[s];
                 c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qs, c0, 0, 0, 0);
                 c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qs, c1, 0, 0, 0);
             }
@@ -1143,7 +1142,6 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
         if (CAUSAL && fast) {
             fast_cut += (unsigned)p_t;
             const int sf = p_t >> 4, zb = p_t - 16 * sf - 4 * g;
-            const bf16x8_t qz = qmask(sf, zb);
             auto tile = [&](auto s0c) {
                 constexpr int S0 = decltype(s0c)::value;
 #pragma unroll
@@ -1151,7 +1149,7 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
                     f32x4_t c0, c1;
                     u32x4 pw;
                     float ls;
-                    scores(kb, S0, qz, c0, c1);
+                    scores(kb, S0, zb, c0, c1);
                     probs(c0, c1, pw, ls);
                     rescale(c0, c1, pw, ls);
                     pv(kb, pw);
@@ -1184,9 +1182,8 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
             const int vlim = CAUSAL ? dq + 1 : a.Sk - jb;  // slot keys below vlim are real keys
             f32x4_t c0, c1;
             const int sf = p_full >> 4, zb = p_full - 16 * sf - 4 * g;
-            const bf16x8_t qz = qmask(sf, zb);
 #define ATF16_S(i) \
-                case i: if constexpr ((i) < NSTEP) scores(kb, (i), qz, c0, c1); break;
+                case i: if constexpr ((i) < NSTEP) scores(kb, (i), zb, c0, c1); break;
             switch (min(sf, NSTEP - 1)) {
                 ATF16_S(0) ATF16_S(1) ATF16_S(2) ATF16_S(3) ATF16_S(4) ATF16_S(5) ATF16_S(6) ATF16_S(7)
                 default: break;
@@ -1196,17 +1193,19 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
                 if (!diag) skipped_u += (unsigned long long)p_lo * 32u * nq;
                 else if (q_valid) skipped += (unsigned long long)p_lo * (unsigned)slots_below16(vlim, kbase_g);
             }
-            for (int p = p_lo; p < p_full; ++p) {
-                const int s = p >> 4, gp = (p >> 2) & 3, w = p & 3;
+            // boundary pairs, step by step so each step's query fragment is a
+            // register known at compile time
+#pragma unroll
+            for (int s = 0; s < NSTEP; ++s)
+            for (int p = max(p_lo, 16 * s); p < min(p_full, 16 * s + 16); ++p) {
+                const int gp = (p >> 2) & 3, w = p & 3;
                 u32x4 k0 = kfrag(kb, 0, s), k1 = kfrag(kb, 1, s);
                 const bool mine = g == gp;
                 k0.x = (mine && w == 0) ? k0.x : 0u; k1.x = (mine && w == 0) ? k1.x : 0u;
                 k0.y = (mine && w == 1) ? k0.y : 0u; k1.y = (mine && w == 1) ? k1.y : 0u;
                 k0.z = (mine && w == 2) ? k0.z : 0u; k1.z = (mine && w == 2) ? k1.z : 0u;
                 k0.w = (mine && w == 3) ? k0.w : 0u; k1.w = (mine && w == 3) ? k1.w : 0u;
-                bf16x8_t qs = qf[0];
-#pragma unroll
-                for (int ss = 1; ss < NSTEP; ++ss) qs = (s == ss) ? qf[ss] : qs;
+                const bf16x8_t qs = qf[s];
                 const f32x4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k0), qs, zero4, 0, 0, 0);
                 const f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qs, zero4, 0, 0, 0);
                 // pair p is kept at slot key c iff |dq - c| <= W_p: lim <= c (<= him)
