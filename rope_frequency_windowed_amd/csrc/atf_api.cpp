@@ -162,9 +162,9 @@ struct DecodePlan {
     int starts[kMaxSplits + 1];
 };
 
-// Decode workgroups resident at once: 2 per CU x 256 CUs; at d = 256 the
-// kernels' registers allow one per CU.
-int64_t decode_resident(int32_t d) { return d == 256 ? 256 : 512; }
+// Decode workgroups resident at once: 2 per CU x 256 CUs (every head dim:
+// at d = 256 the kernels take 16-key chunks so that two fit).
+int64_t decode_resident(int32_t) { return 512; }
 
 int decode_nsplit(int32_t B, int32_t Hq, int32_t Hkv, int64_t S, int32_t d) {
     const int group = Hq / Hkv;

@@ -1403,15 +1403,36 @@ __device__ inline u32x2 lds_read_tr16(const unsigned char *lds, unsigned byte_ad
     return __builtin_bit_cast(u32x2, r);
 }
 
+// One 16-dim block of O^T += V^T P^T over a wave's chunk.  Two 16-key groups:
+// MFMA 16x16x32, K index 8q + 4g + c = key 16g + 4q + c of the chunk (the
+// probability words of both groups, and the value reads of both, side by
+// side).  One group: MFMA 16x16x16 over keys 4q + c.
+template <int NG>
+__device__ inline f32x4_t decode_pv(const unsigned char *vb, unsigned addr0, unsigned addr1,
+                                    const unsigned (&pw)[2 * NG], f32x4_t o) {
+    const u32x2 v0 = lds_read_tr16(vb, addr0);
+    if constexpr (NG == 2) {
+        const u32x2 v1 = lds_read_tr16(vb, addr1);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}),
+                                                       __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]}),
+                                                       o, 0, 0, 0);
+    } else {
+        (void)addr1;
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, v0),
+                                                         __builtin_bit_cast(s16x4_t, (u32x2){pw[0], pw[1]}), o, 0, 0, 0);
+    }
+}
+
 template <int D, bool GPTJ>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, D >= 256 ? 2 : 1) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
-    constexpr int CK = 32;               // keys per wave chunk
+    constexpr int CK = (D >= 256) ? 16 : 32;  // keys per wave chunk (d = 256: half, for two workgroups per CU)
+    constexpr int NG = CK / 16;          // 16-key groups per chunk
     constexpr int VROW = D * 2;          // bytes per value row
     constexpr int CHV = VROW / 16;       // 16-byte chunks per value row
-    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128)
+    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128 and 256)
     constexpr int VR = 1024 / VROW;      // value rows per 1 KB direct-load piece
     constexpr int H = kDecodeHeads;
     __shared__ float2 fine[P][CK];       // cos/sin(u * theta_p), u = 0..31
@@ -1513,10 +1534,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             const int wpp = window_at(win, pp);                                       \
             if (wpp >= d_far_) break;                                                 \
             ps0_ += (wpp < a.S - ((jc_) + t)) ? 1 : 0;                                \
-            ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;                           \
+            if (NG > 1) ps1_ += (wpp < a.S - ((jc_) + 16 + t)) ? 1 : 0;               \
         }                                                                             \
         if ((jc_) + t >= ke) ps0_ = P;                                                \
-        if ((jc_) + 16 + t >= ke) ps1_ = P;                                           \
+        if (NG > 1 && (jc_) + 16 + t >= ke) ps1_ = P;                                 \
     }
     // Key pieces of the last two K-steps (the only ones far keys keep) are
     // loaded one chunk ahead into registers; nearer steps load on use.  Every
@@ -1528,7 +1549,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int SPRE = (NSTEP >= 2) ? NSTEP - 2 : 0;
 #define DEC_LOAD_K(jc_, ps0_, ps1_)                                                     \
     {                                                                                 \
-        _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
+        _Pragma("unroll") for (int g = 0; g < NG; ++g) {                              \
             const int psg_ = g ? (ps1_) : (ps0_);                                     \
             const unsigned short *kr_ = kbase + (long long)min((jc_) + 16 * g + t, ke - 1) * D; \
             _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i) {                \
@@ -1541,7 +1562,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 
     int j0 = ks + wave * CK;
     int s_min = 0, ps0 = P, ps1 = P;
-    u32x2 klo[2][NSTEP - SPRE], khi[2][NSTEP - SPRE];
+    u32x2 klo[NG][NSTEP - SPRE], khi[NG][NSTEP - SPRE];
     if (j0 < ke) {
         DEC_LOAD_V(j0);
         DEC_CHUNK_KEYS(j0, s_min, ps0, ps1);
@@ -1584,9 +1605,9 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        f32x4_t sc[2];
+        f32x4_t sc[NG];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
             const int u = 16 * g + t;  // key offset in the chunk
             const int ps = g ? ps1 : ps0;
             if (q == 0 && ps < P) skipped += (unsigned long long)ps * (unsigned)nh;
@@ -1633,8 +1654,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
         }
 
         // online softmax per head slot t (log2 units, lazy reference)
-        float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        float bm = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+        if (NG > 1) bm = fmaxf(bm, fmaxf(fmaxf(sc[NG - 1][0], sc[NG - 1][1]), fmaxf(sc[NG - 1][2], sc[NG - 1][3])));
         bm = quad_max(bm);
         const bool move = first || bm > m_ref + kRescale;
         first = false;
@@ -1646,27 +1667,21 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= corr;
         }
-        unsigned pw[4];
+        unsigned pw[2 * NG];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
             pw[2 * g] = pack_bf(fast_exp2(sc[g][0] - m_ref), fast_exp2(sc[g][1] - m_ref));
             pw[2 * g + 1] = pack_bf(fast_exp2(sc[g][2] - m_ref), fast_exp2(sc[g][3] - m_ref));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
-        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+        for (int i = 0; i < 2 * NG; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
 
         // P.V on this chunk's values (written to LDS by this wave above)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const u32x2 v0 = lds_read_tr16(vb, vtr_addr(db, 0));
-            const u32x2 v1 = lds_read_tr16(vb, vtr_addr(db, 1));
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}), pop, o[db], 0, 0, 0);
-        }
+        for (int db = 0; db < NDB; ++db) o[db] = decode_pv<NG>(vb, vtr_addr(db, 0), vtr_addr(db, NG - 1), pw, o[db]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1908,14 +1923,15 @@ __global__ __launch_bounds__(256) void paged_write_bf16_kernel(PagedWriteArgs a)
 // ============================================================================
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, D >= 256 ? 2 : 1) void decode_kcache_bf16_kernel(DecodeArgs a) {
     constexpr int P = D / 2;
     constexpr int NSTEP = D / 32;        // score K-steps of 16 pairs
     constexpr int NDB = D / 16;          // P.V output blocks of 16 dims
-    constexpr int CK = 32;               // keys per wave chunk
+    constexpr int CK = (D >= 256) ? 16 : 32;  // keys per wave chunk (d = 256: half, for two workgroups per CU)
+    constexpr int NG = CK / 16;          // 16-key groups per chunk
     constexpr int VROW = D * 2;          // bytes per value row
     constexpr int CHV = VROW / 16;       // 16-byte chunks per value row
-    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128)
+    constexpr int VBYTES = CK * VROW;    // value chunk bytes (8 KB at d = 128 and 256)
     constexpr int VR = 1024 / VROW;      // value rows per 1 KB direct-load piece
     constexpr int H = kDecodeHeads;
     constexpr unsigned KPBLK = (P / 4) * 1024;  // bytes of one 64-key block of the key cache
@@ -2076,10 +2092,10 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
             const int wpp = window_at(win, pp);                                       \
             if (wpp >= d_far_) break;                                                 \
             ps0_ += (wpp < S - ((jc_) + t)) ? 1 : 0;                                  \
-            ps1_ += (wpp < S - ((jc_) + 16 + t)) ? 1 : 0;                             \
+            if (NG > 1) ps1_ += (wpp < S - ((jc_) + 16 + t)) ? 1 : 0;                 \
         }                                                                             \
         if ((jc_) + t >= ke) ps0_ = P;                                                \
-        if ((jc_) + 16 + t >= ke) ps1_ = P;                                           \
+        if (NG > 1 && (jc_) + 16 + t >= ke) ps1_ = P;                                 \
     }
     // Key planes of the last two K-steps (the only ones far keys keep) are
     // loaded one chunk ahead into registers; nearer steps load on use.  A lane
@@ -2091,7 +2107,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 #define DEC_LOAD_K(jc_, sl_)                                                            \
     {                                                                                 \
         const __amdgpu_buffer_rsrc_t kr_ = raw_rsrc(kblock(sl_), KPBLK);              \
-        _Pragma("unroll") for (int g = 0; g < 2; ++g) {                               \
+        _Pragma("unroll") for (int g = 0; g < NG; ++g) {                              \
             const int row_ = min((jc_) + 16 * g + t, ke - 1) % kKeyTile;               \
             _Pragma("unroll") for (int i = 0; i < NSTEP - SPRE; ++i)                  \
                 kreg[g][i] = raw_load16(kr_, DEC_KOFF(4 * (SPRE + i) + q, row_));     \
@@ -2100,7 +2116,7 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 
     int j0 = ks + wave * CK;
     int s_min = 0, ps0 = P, ps1 = P, pmin = 0;
-    u32x4 kreg[2][NSTEP - SPRE];
+    u32x4 kreg[NG][NSTEP - SPRE];
     long long sl_cur = 0, sl_nxt = 0;
     if (j0 < ke) {
         sl_cur = slot_of(j0 / kKeyTile);
@@ -2120,9 +2136,9 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         if (jn < ke) DEC_LOAD_V(jn, sl_nxt);
         const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kblock(sl_cur), KPBLK);
 
-        f32x4_t sc[2];
+        f32x4_t sc[NG];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
             const int u = 16 * g + t;  // key offset in the chunk
             const int ps = g ? ps1 : ps0;
             if (q == 0 && ps < P) skipped += (unsigned long long)ps * (unsigned)nh;
@@ -2152,8 +2168,8 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
         }
 
         // online softmax per head slot t (log2 units, lazy reference)
-        float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        float bm = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+        if (NG > 1) bm = fmaxf(bm, fmaxf(fmaxf(sc[NG - 1][0], sc[NG - 1][1]), fmaxf(sc[NG - 1][2], sc[NG - 1][3])));
         bm = quad_max(bm);
         const bool move = first || bm > m_ref + kRescale;
         first = false;
@@ -2165,27 +2181,21 @@ __global__ __launch_bounds__(256) void decode_kcache_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= corr;
         }
-        unsigned pw[4];
+        unsigned pw[2 * NG];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) {
             pw[2 * g] = pack_bf(fast_exp2(sc[g][0] - m_ref), fast_exp2(sc[g][1] - m_ref));
             pw[2 * g + 1] = pack_bf(fast_exp2(sc[g][2] - m_ref), fast_exp2(sc[g][3] - m_ref));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
-        const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+        for (int i = 0; i < 2 * NG; ++i) l_run = dot2_bf(pw[i], kOnesBf16x2, l_run);
 
         // P.V on this chunk's values (written to LDS by this wave above)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const u32x2 v0 = lds_read_tr16(vb, vtr_addr(db, 0));
-            const u32x2 v1 = lds_read_tr16(vb, vtr_addr(db, 1));
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, (u32x4){v0.x, v0.y, v1.x, v1.y}), pop, o[db], 0, 0, 0);
-        }
+        for (int db = 0; db < NDB; ++db) o[db] = decode_pv<NG>(vb, vtr_addr(db, 0), vtr_addr(db, NG - 1), pw, o[db]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
