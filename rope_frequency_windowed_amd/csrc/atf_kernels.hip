@@ -484,16 +484,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     static_assert(D <= 128, "d = 256 has its own kernel");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
 
-    // ---- work item: longest query tiles first; the group heads sharing one kv
-    // head run on one XCD (workgroup ids are dealt to the 8 XCDs round robin).
+    // ---- work unit u = (key split sp, work item gi), split-major, longest
+    // query tiles first within a split.  Workgroup ids are dealt to the 8 XCDs
+    // round robin; unit u runs on XCD u % 8 with its group workgroups (the
+    // heads sharing one kv head), so K/V tiles are reused in that XCD's L2;
+    // when the work items do not fill the 8 XCDs, consecutive splits of a
+    // short chunk go to the others.
     // A work item is QT query rows of one head (wave w: rows 32 w ..), or, head
     // packed (a.hpack, for short chunks), 32 query rows of up to NW heads that
     // share the kv head (wave w: head NW * slab + w of the group, the same
     // rows), so one LDS key tile serves NW heads; a.group then counts slabs.
     const int L = blockIdx.x;
     const int xcd = L & 7, slot = L >> 3;
-    const int gi = (slot / a.group) * 8 + xcd;
-    if (gi >= a.n_groups) return;
+    const int u = (slot / a.group) * 8 + xcd;
+    if (u >= a.n_groups * a.n_ksplit) return;
+    const int gi = u % a.n_groups, sp = u / a.n_groups;
     const int g = slot % a.group;
     const int per_qt = a.B * a.Hkv;
     const int qt = a.n_qtiles - 1 - gi / per_qt;
@@ -552,7 +557,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
     // key tiles of this workgroup's split of the key range: [kt0, kt1)
-    const int sp = blockIdx.y;
     const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
@@ -925,10 +929,11 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     static_assert(NW % 2 == 0, "swz8 repeats every 16 value rows (2 KB): the piece stride must keep it");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILE_BYTES];
 
-    const int L = blockIdx.x;
+    const int L = blockIdx.x;  // work units and XCD placement as in the 32x32 kernel
     const int xcd = L & 7, slot = L >> 3;
-    const int gi = (slot / a.group) * 8 + xcd;
-    if (gi >= a.n_groups) return;
+    const int u = (slot / a.group) * 8 + xcd;
+    if (u >= a.n_groups * a.n_ksplit) return;
+    const int gi = u % a.n_groups, sp = u / a.n_groups;
     const int hs = slot % a.group;  // head in the group, or (head packed) slab of NW heads
     const int per_qt = a.B * a.Hkv;
     const int qt = a.n_qtiles - 1 - gi / per_qt;
@@ -982,7 +987,6 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
     // key tiles of this workgroup's split of the key range: [kt0, kt1)
-    const int sp = blockIdx.y;
     const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
 
     // Tile loader: piece m (1 KB) of K' lands lane-linear at LDS byte 1024 m +
@@ -2347,8 +2351,8 @@ hipError_t launch_prep_f32(const PrepArgs &a, int, hipStream_t s) {
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
-    // x: (query tile, kv head, XCD slot) work items; y: split of the key range
-    const dim3 grid((unsigned)(((a.n_groups + 7) / 8) * 8 * a.group), (unsigned)a.n_ksplit);
+    // one workgroup per (work item, key split, head or slab), dealt to XCDs
+    const dim3 grid((unsigned)(((a.n_groups * a.n_ksplit + 7) / 8) * 8 * a.group));
     if (d == 256) {
         if (a.causal) prefill16_bf16_kernel<256, true><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
         else prefill16_bf16_kernel<256, false><<<grid, kPrefill16Waves * 64, 0, s>>>(a);
