@@ -840,26 +840,36 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     // ---- epilogue: O / l, bf16, store (lane holds dims 32db + 8g + 4*half + 0..3).
     // A key-range split instead writes its unnormalised O, m_ref and l (m =
     // -inf when the split holds none of the query's mass) for the combine.
+    // Non-causal (at the register limit): the row and head are recomputed
+    // from the lane id and the uniform wave index, so no per-lane prologue
+    // value stays live across its tile loop.
     const float l_tot = partner_sum(l_run);
+    {
+    const int lane_e = CAUSAL ? lane : (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int half_e = CAUSAL ? half : lane_e >> 5;
+    const int hw_e = a.hpack ? NW * g + wave_s : 0;
+    const int h_e = CAUSAL ? h : a.hpack ? hk * hgroup + min(hw_e, hgroup - 1) : hk * a.group + g;
+    const int my_q_e = CAUSAL ? my_q : (a.hpack ? qt * 32 : qt * QT + wave_s * 32) + (lane_e & 31);
+    const bool q_valid_e = CAUSAL ? q_valid : my_q_e < a.Sq && hw_e < hgroup;
     if (a.n_ksplit > 1) {
-        if (q_valid) {
-            float *pr = a.part + ((((long long)(b * a.Hq + h) * a.Sq + my_q) * a.n_ksplit) + sp) * (D + 2);
+        if (q_valid_e) {
+            float *pr = a.part + ((((long long)(b * a.Hq + h_e) * a.Sq + my_q_e) * a.n_ksplit) + sp) * (D + 2);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {  // rows of d + 2 floats are 8-byte aligned
-                    float *pd = pr + 32 * db + 8 * g4 + 4 * half;
+                    float *pd = pr + 32 * db + 8 * g4 + 4 * half_e;
                     *(float2 *)pd = make_float2(o[db][4 * g4], o[db][4 * g4 + 1]);
                     *(float2 *)(pd + 2) = make_float2(o[db][4 * g4 + 2], o[db][4 * g4 + 3]);
                 }
-            if (half == 0) {
+            if (half_e == 0) {
                 pr[D] = l_tot > 0.f ? m_ref : -INFINITY;
                 pr[D + 1] = l_tot;
             }
         }
-    } else if (q_valid) {
+    } else if (q_valid_e) {
         const float inv = 1.f / l_tot;
-        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h_e) * a.Sq + my_q_e) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -867,12 +877,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                 u32x2 w;
                 w.x = pack_bf(o[db][4 * g4 + 0] * inv, o[db][4 * g4 + 1] * inv);
                 w.y = pack_bf(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv);
-                *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half) = w;
+                *(u32x2 *)(orow + 32 * db + 8 * g4 + 4 * half_e) = w;
             }
     }
     skipped_u += (unsigned long long)fast_cut * (NB * 16u) * n_valid;
     skipped = wave_sum_u64(skipped) + skipped_u;
-    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+    if (lane_e == 0 && skipped) atomicAdd(a.counter, skipped);
+    }
 }
 
 // ============================================================================
@@ -1245,35 +1256,45 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
 #undef ATF16_TILE_LOAD
 
     // epilogue: lane (t, g) holds dims 16 db + 4 g + (0..3) of query t; a
-    // key-range split writes its unnormalised O, m_ref and l for the combine
+    // key-range split writes its unnormalised O, m_ref and l for the combine.
+    // The row and head are recomputed from the lane id and the uniform wave
+    // index, so no per-lane prologue value stays live across the tile loop.
     const float l_tot = quad_sum(l_run);
+    {
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int t_e = lane_e & 15, g_e = lane_e >> 4;
+    const int hw_e = a.hpack ? NW * hs + wave_s : 0;
+    const int h_e = a.hpack ? hk * hgroup + min(hw_e, hgroup - 1) : hk * a.group + hs;
+    const int my_q_e = (a.hpack ? qt * 16 : qt * QT + wave_s * 16) + t_e;
+    const bool q_valid_e = my_q_e < a.Sq && hw_e < hgroup;
     if (a.n_ksplit > 1) {
-        if (q_valid) {
-            float *pr = a.part + ((((long long)(b * a.Hq + h) * a.Sq + my_q) * a.n_ksplit) + sp) * (D + 2);
+        if (q_valid_e) {
+            float *pr = a.part + ((((long long)(b * a.Hq + h_e) * a.Sq + my_q_e) * a.n_ksplit) + sp) * (D + 2);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {  // rows of d + 2 floats are 8-byte aligned
-                *(float2 *)(pr + 16 * db + 4 * g) = make_float2(o[db][0], o[db][1]);
-                *(float2 *)(pr + 16 * db + 4 * g + 2) = make_float2(o[db][2], o[db][3]);
+                *(float2 *)(pr + 16 * db + 4 * g_e) = make_float2(o[db][0], o[db][1]);
+                *(float2 *)(pr + 16 * db + 4 * g_e + 2) = make_float2(o[db][2], o[db][3]);
             }
-            if (g == 0) {
+            if (g_e == 0) {
                 pr[D] = l_tot > 0.f ? m_ref : -INFINITY;
                 pr[D + 1] = l_tot;
             }
         }
-    } else if (q_valid) {
+    } else if (q_valid_e) {
         const float inv = 1.f / l_tot;
-        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
+        unsigned short *orow = (unsigned short *)a.out + ((long long)(b * a.Hq + h_e) * a.Sq + my_q_e) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
             u32x2 w;
             w.x = pack_bf(o[db][0] * inv, o[db][1] * inv);
             w.y = pack_bf(o[db][2] * inv, o[db][3] * inv);
-            *(u32x2 *)(orow + 16 * db + 4 * g) = w;
+            *(u32x2 *)(orow + 16 * db + 4 * g_e) = w;
         }
     }
     skipped_u += (unsigned long long)fast_cut * (NB * 32u) * nq;
     skipped = wave_sum_u64(skipped) + skipped_u;
-    if (lane == 0 && skipped) atomicAdd(a.counter, skipped);
+    if (lane_e == 0 && skipped) atomicAdd(a.counter, skipped);
+    }
 }
 
 // ============================================================================
