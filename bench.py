@@ -43,6 +43,8 @@ KCACHE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kcache_kv262144_co
 PAGED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_paged_kv262144_counters.txt")
 GPTJ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gptj_kv262144_counters.txt")
 D256_DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_d256_kv65536_counters.txt")
+SQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_sq_counters.txt")
+N_SIMD, CLOCK_HZ = 1024, 2.4e9   # MI355X: 256 CUs x 4 SIMDs, peak engine clock
 
 PREFILL = dict(B=1, Hq=28, Hkv=4, S=131072, d=128, base=1e6, alpha=1.0)
 DECODE = dict(B=8, Hq=28, Hkv=4, S=262144, d=128, base=1e6, alpha=1.0)
@@ -76,10 +78,9 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(path=COUNTERS_FILE):
-    """Counter-measured HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each
-    scaled by what the same counter reads for a 1 GiB copy), if the summary
-    was taken on the current kernel source; else None."""
+def read_summary(path):
+    """The `key: value` lines of a profiles/ summary, if it was taken on the
+    current kernel source; else None."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -90,8 +91,36 @@ def read_traffic(path=COUNTERS_FILE):
                 vals[k.strip()] = v.split()[0] if v.split() else ""
     if vals.get("kernel_source_sha256_16") != source_hash():
         return None
+    return vals
+
+
+def read_traffic(path=COUNTERS_FILE):
+    """Counter-measured HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what the same counter reads for a 1 GiB copy), if the summary
+    was taken on the current kernel source; else None."""
+    vals = read_summary(path)
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["hbm_bytes_per_launch"]) if vals else None
+    except (KeyError, ValueError):
+        return None
+
+
+def mfma_busy(kernel_ms, path=SQ_COUNTERS_FILE):
+    """How busy the MFMA pipes are during the prefill kernel: the counted
+    SQ_VALU_MFMA_BUSY_CYCLES of one launch (summary taken on the current
+    kernel source) over 1024 SIMDs x 2.4 GHz x the kernel time measured here;
+    None without such a summary."""
+    vals = read_summary(path)
+    if not vals:
+        return None
+    try:
+        cyc = float(vals["mfma_busy_cycles_per_launch"])
+        return {"frac": cyc / (N_SIMD * CLOCK_HZ * kernel_ms * 1e-3), "busy_cycles_per_launch": cyc,
+                "frac_of_busy_cycles": float(vals["mfma_busy_frac_of_busy_cycles"]),
+                "mfma_insts_per_wave_block": float(vals["mfma_insts_per_wave_block"]),
+                "valu_insts_per_wave_block": float(vals["valu_insts_per_wave_block"]),
+                "wave_blocks_per_launch": int(vals["wave_blocks_per_launch"]),
+                "source": os.path.relpath(path, ROOT)}
     except (KeyError, ValueError):
         return None
 
@@ -577,7 +606,8 @@ def main():
         res["unit"] = "tok/s"
         res["roofline"] = attain({"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                                  "traffic": read_traffic(), "kernel": "prefill_bf16_kernel<128>",
+                                  "traffic": read_traffic(), "mfma_busy": mfma_busy(attend_ms),
+                                  "kernel": "prefill_bf16_kernel<128>",
                                   "kernel_ms": attend_ms, "algorithmic_flops_per_launch": flops})
         config["prefill"] = dict(PREFILL, prep_ms=prep_ms, attend_ms=attend_ms, attend_ms_median=attend_med,
                                  attend_ms_min=attend_min,
