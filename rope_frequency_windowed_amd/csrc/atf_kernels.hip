@@ -17,6 +17,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 
 namespace atf {
@@ -627,7 +628,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     s16x4_t negm_b = __builtin_bit_cast(s16x4_t, (u32x2){0u, 0u});
     // dropped-term count: per lane where it differs between lanes, uniform
     // (whole-block) contributions in skipped_u
-    unsigned long long skipped = 0, skipped_u = 0;
+    // (non-causal, at the register limit: a lane's boundary-term count fits
+    // 32 bits, since a wave meets at most two general tiles per window plus
+    // the diagonal and last ones, each adding at most 4 x 16 x P terms)
+    using lane_cnt_t = std::conditional_t<CAUSAL, unsigned long long, unsigned>;
+    lane_cnt_t skipped = 0;
+    unsigned long long skipped_u = 0;
     unsigned fast_cut = 0;  // sum of the pair cut over fast tiles (x NB x 16 x n_valid at the end)
     const unsigned n_valid = (unsigned)__builtin_popcountll(__ballot(q_valid));
     const f32x16_t zero16 = {};
@@ -762,7 +768,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
                 if (!diag) {                                                                      \
                     skipped_u += (unsigned long long)p_lo[kb] * 16u * n_valid;                    \
                 } else if (q_valid) {                                                             \
-                    skipped += (unsigned long long)p_lo[kb] * (unsigned)keys_below(vlim);         \
+                    skipped += (lane_cnt_t)p_lo[kb] * (unsigned)keys_below(vlim);                 \
                 }                                                                                 \
             }                                                                                     \
             if (p_lo[kb] < p_full[kb]) {                                                          \
@@ -881,8 +887,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             }
     }
     skipped_u += (unsigned long long)fast_cut * (NB * 16u) * n_valid;
-    skipped = wave_sum_u64(skipped) + skipped_u;
-    if (lane_e == 0 && skipped) atomicAdd(a.counter, skipped);
+    const unsigned long long total = wave_sum_u64((unsigned long long)skipped) + skipped_u;
+    if (lane_e == 0 && total) atomicAdd(a.counter, total);
     }
 }
 
@@ -1045,7 +1051,11 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     // so scores leave the chain shifted by the reference (a lane's 4 elements
     // all belong to its query t)
     f32x4_t negm = {0.f, 0.f, 0.f, 0.f};
-    unsigned long long skipped = 0, skipped_u = 0;
+    // a lane's boundary-term count fits 32 bits: a wave meets at most two
+    // general tiles per window plus the diagonal and last ones, each adding
+    // at most 2 x 8 x P terms
+    unsigned skipped = 0;
+    unsigned long long skipped_u = 0;
     unsigned fast_cut = 0;
     const unsigned nq = (unsigned)__builtin_popcountll(__ballot(q_valid && g == 0));
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -1206,7 +1216,7 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
 #undef ATF16_S
             if (p_lo > 0) {
                 if (!diag) skipped_u += (unsigned long long)p_lo * 32u * nq;
-                else if (q_valid) skipped += (unsigned long long)p_lo * (unsigned)slots_below16(vlim, kbase_g);
+                else if (q_valid) skipped += (unsigned)p_lo * (unsigned)slots_below16(vlim, kbase_g);
             }
             // boundary pairs, step by step so each step's query fragment is a
             // register known at compile time
@@ -1292,8 +1302,8 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
         }
     }
     skipped_u += (unsigned long long)fast_cut * (NB * 32u) * nq;
-    skipped = wave_sum_u64(skipped) + skipped_u;
-    if (lane_e == 0 && skipped) atomicAdd(a.counter, skipped);
+    const unsigned long long total = wave_sum_u64((unsigned long long)skipped) + skipped_u;
+    if (lane_e == 0 && total) atomicAdd(a.counter, total);
     }
 }
 
