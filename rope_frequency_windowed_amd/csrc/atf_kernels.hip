@@ -638,6 +638,15 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned n_valid = (unsigned)__builtin_popcountll(__ballot(q_valid));
     const f32x16_t zero16 = {};
     const int koff0 = 4 * half;
+    // non-causal (at the register limit): my_qk - koff0 recomputed from the
+    // lane id where the boundary path needs it rather than held across the
+    // tile loop; the empty move keeps the compiler from hoisting it back out
+    auto nc_dq_base = [&]() {
+        int z;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, (unsigned)z));
+        return i0k + (ln & 31) - 4 * (ln >> 5);
+    };
     // per-lane LDS byte offsets (swizzle folded in)
     const unsigned krow0 = (unsigned)qi;  // key row of block 0; block 1 is +32 rows
     const unsigned kbase_lane = krow0 * (CH * 16);
@@ -762,7 +771,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             const unsigned kbase = kbase_lane + 32u * (kb) * (CH * 16);                           \
             /* element r holds key jb + koff0 + c_r, c_r = 8(r/4) + r%4, at distance dq - c_r;    \
                it is a real (causal) key iff c_r < vlim */                                        \
-            const int dq = my_qk - koff0 - jb;                                                    \
+            const int dq = (CAUSAL ? my_qk - koff0 : nc_dq_base()) - jb;                          \
             const int vlim = CAUSAL ? dq + 1 : a.Sk - jb - koff0;                                 \
             if (p_lo[kb] > 0) {                                                                   \
                 if (!diag) {                                                                      \
