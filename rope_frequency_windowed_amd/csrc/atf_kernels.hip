@@ -1233,7 +1233,11 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
             for (int s = 0; s < NSTEP; ++s)
             for (int p = max(p_lo, 16 * s); p < min(p_full, 16 * s + 16); ++p) {
                 const int gp = (p >> 2) & 3, w = p & 3;
-                u32x4 k0 = kfrag(kb, 0, s), k1 = kfrag(kb, 1, s);
+                // (an opaque zero in the address keeps these reads from being
+                // merged with the score chain's reads of the same step)
+                int z;
+                asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+                u32x4 k0 = kfrag(kb, 0, s + z), k1 = kfrag(kb, 1, s + z);
                 const bool mine = g == gp;
                 k0.x = (mine && w == 0) ? k0.x : 0u; k1.x = (mine && w == 0) ? k1.x : 0u;
                 k0.y = (mine && w == 1) ? k0.y : 0u; k1.y = (mine && w == 1) ? k1.y : 0u;
