@@ -379,16 +379,20 @@ __device__ inline int keys_below(int x) {
 }
 
 // Probabilities 2^s of one 32x32 score block (a lane's 16 keys) as 8 bf16
-// pairs, and their sum as the MFMA will see them (the rounded values).
+// pairs, and their sum, taken in fp32 before the rounding.  The sum is a tree
+// of fp32 adds, which issue beside the P.V MFMAs; v_dot2 over the rounded
+// pairs (the sum exactly as the MFMA sees it) does not overlap MFMAs on
+// gfx950 and cost about 1% of the kernel.
 __device__ __attribute__((always_inline)) inline void block_probs(const f32x16_t &s, unsigned (&pw)[8],
                                                                    float &lsum) {
-    constexpr unsigned kOnes = 0x3f803f80u;  // (1.0, 1.0) in bf16
-    lsum = 0.f;
+    float t[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        pw[u] = pack_bf(fast_exp2(s[2 * u]), fast_exp2(s[2 * u + 1]));
-        lsum = dot2_bf(pw[u], kOnes, lsum);
+        const float e0 = fast_exp2(s[2 * u]), e1 = fast_exp2(s[2 * u + 1]);
+        pw[u] = pack_bf(e0, e1);
+        t[u] = e0 + e1;
     }
+    lsum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
 }
 
 // O^T += V^T P^T for one 32-key block of the tile in LDS (lt): two K-steps
@@ -1053,7 +1057,6 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     constexpr float kSumLimit = 4096.f;
-    constexpr unsigned kOnes = 0x3f803f80u;
     float m_ref = 0.f, l_run = 0.f;
     bool first = true;
     // -m_ref in every element: the first score MFMA of a block starts from it,
@@ -1114,15 +1117,19 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
                 c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k1), qs, c1, 0, 0, 0);
             }
         };
+        // the sum in fp32 before the rounding, as in the 32x32 kernel's block_probs
         auto probs = [&](const f32x4_t &c0, const f32x4_t &c1, u32x4 &pw, float &ls) {
-            pw.x = pack_bf(fast_exp2(c0[0]), fast_exp2(c0[1]));
-            pw.y = pack_bf(fast_exp2(c0[2]), fast_exp2(c0[3]));
-            pw.z = pack_bf(fast_exp2(c1[0]), fast_exp2(c1[1]));
-            pw.w = pack_bf(fast_exp2(c1[2]), fast_exp2(c1[3]));
-            ls = dot2_bf(pw.x, kOnes, 0.f);
-            ls = dot2_bf(pw.y, kOnes, ls);
-            ls = dot2_bf(pw.z, kOnes, ls);
-            ls = dot2_bf(pw.w, kOnes, ls);
+            float e[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                e[r] = fast_exp2(c0[r]);
+                e[4 + r] = fast_exp2(c1[r]);
+            }
+            pw.x = pack_bf(e[0], e[1]);
+            pw.y = pack_bf(e[2], e[3]);
+            pw.z = pack_bf(e[4], e[5]);
+            pw.w = pack_bf(e[6], e[7]);
+            ls = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
         };
         // move the reference when a lane's block sum overflows (or at the first block)
         auto rescale = [&](f32x4_t &c0, f32x4_t &c1, u32x4 &pw, float &ls) {
