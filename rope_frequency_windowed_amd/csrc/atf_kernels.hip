@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
         v_goff = (unsigned)(vrow * 128 + ((((kbyte / 16) & 7) ^ swz8(vrow)) * 16));
     }
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-#define ATF_TILE_LOAD(kt_, buf_)                                                           \
+#define ATF_TILE_LOAD(kt_, buf_, part_)                                                    \
     {                                                                                      \
         const int j0_ = (kt_) * KT;                                                        \
         const int dmin_wg_ = CAUSAL ? max(0, q0k - (j0_ + KT - 1))                         \
@@ -607,8 +607,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
         const __amdgpu_buffer_rsrc_t vr_ = raw_rsrc(vg + (long long)j0_ * (D * 2), KT_BYTES); \
         unsigned char *lk_ = lds + (buf_) * TILE_BYTES + wave_s * 1024;                    \
         _Pragma("unroll") for (int n = 0; n < NLD; ++n) {                                  \
-            lds_dma16_buf(kr_, koff_[n % KPER], n * NW * 1024, lk_ + n * NW * 1024);       \
-            lds_dma16_buf(vr_, v_goff, n * NW * 1024, lk_ + KT_BYTES + n * NW * 1024);     \
+            if ((part_) & 1) lds_dma16_buf(kr_, koff_[n % KPER], n * NW * 1024, lk_ + n * NW * 1024); \
+            if ((part_) & 2) lds_dma16_buf(vr_, v_goff, n * NW * 1024, lk_ + KT_BYTES + n * NW * 1024); \
         }                                                                                  \
     }
 
@@ -658,13 +658,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned vbase_lane = KT_BYTES + (unsigned)qi * 128;
     const unsigned vz = (unsigned)((swz8(qi) ^ half) << 4);
 
-    if (kt0 < kt1) ATF_TILE_LOAD(kt0, 0);
+    if (kt0 < kt1) ATF_TILE_LOAD(kt0, 0, 3);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int kt = kt0; kt < kt1; ++kt) {
         const int buf = (kt - kt0) & 1;
-        if (kt + 1 < kt1) ATF_TILE_LOAD(kt + 1, buf ^ 1);
+        const bool more = kt + 1 < kt1;
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * KT;
 
@@ -732,14 +732,20 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             p_t = cut_below(win, dmax);
             fast = fast && plo_t == p_t;
         }
+        // The next tile's loads: on fast tiles its keys after the first block
+        // pair's score chains and its values after that pair, rather than
+        // both at the tile start, where every wave's first chains read the
+        // keys of this tile.
         if (fast) {
             fast_cut += (unsigned)p_t;
             const int sf = p_t >> 3, zb = p_t - 8 * sf - koff0;
 #pragma unroll
             for (int kp = 0; kp < NB; kp += 2) {
+                if (kp == 2 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 2);
                 const unsigned char *lv = lt + (kp >> 1) * (D * 128);
                 qk_pair<NSTEP>(sf, lt, kbase_lane + 32u * kp * (CH * 16), kbase_lane + 32u * (kp + 1) * (CH * 16), ky,
                                qf, zb, ones_a, negm_b, sacc[0], sacc[1], pw[0], lsum[0]);
+                if (kp == 0 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 1);
                 ATF_BLOCK_RESCALE(0, true)
                 block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
                 block_probs(sacc[1], pw[1], lsum[1]);
@@ -751,6 +757,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             continue;
         }
 
+        if (more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 3);
         int p_lo[NB], p_full[NB];
         bool live[NB];
 #pragma unroll
