@@ -18,8 +18,6 @@ window is unbounded, so it is kept at every distance):
   overflows fp32 unless the reference moves before P.V; queries that see it
   must return that key's value.
 """
-import math
-
 import numpy as np
 import pytest
 
