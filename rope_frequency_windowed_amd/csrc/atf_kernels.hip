@@ -741,11 +741,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             const int sf = p_t >> 3, zb = p_t - 8 * sf - koff0;
 #pragma unroll
             for (int kp = 0; kp < NB; kp += 2) {
-                if (kp == 2 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 2);
+                if (NB > 2 && kp == 2 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 2);
                 const unsigned char *lv = lt + (kp >> 1) * (D * 128);
                 qk_pair<NSTEP>(sf, lt, kbase_lane + 32u * kp * (CH * 16), kbase_lane + 32u * (kp + 1) * (CH * 16), ky,
                                qf, zb, ones_a, negm_b, sacc[0], sacc[1], pw[0], lsum[0]);
-                if (kp == 0 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 1);
+                // (a one-pair tile takes its values here too)
+                if (kp == 0 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, NB > 2 ? 1 : 3);
                 ATF_BLOCK_RESCALE(0, true)
                 block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
                 block_probs(sacc[1], pw[1], lsum[1]);
