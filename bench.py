@@ -341,12 +341,26 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
     n_c = Sq * (Sk - Sq) + Sq * (Sq + 1) // 2
     flops = P["B"] * P["Hq"] * (4 * (d // 2) * n_c + 2 * d * n_c) - 4 * got
     tf = flops / (ms * 1e-3) / 1e12
+    # 16 queries over 131072 keys do about 110 flops per algorithmic byte,
+    # below the bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312): the step is bound by
+    # HBM.  Algorithmic bytes: the kept key pairs of each key at its distance
+    # from the chunk's first query (key j keeps pair p iff Sk - Sq - j <= W_p:
+    # min(Sk, Sq + W_p) keys per pair) and every value row, per kv head; the
+    # 16 appended keys and values read and written; q and out.
+    W = atf.atf_window_table(d, P["base"], P["alpha"])
+    kept = sum(min(Sk, Sq + int(w)) for w in W)
+    nbytes = (P["B"] * P["Hkv"] * (4 * kept + 2 * d * Sk) + P["B"] * P["Hkv"] * Sq * d * 2 * 4
+              + 2 * P["B"] * P["Hq"] * Sq * d * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
     out["prefill_chunk_cached_sq16"] = {
         "value": P["B"] * Sq / (ms * 1e-3), "unit": "tok/s (append 16 keys to the kept cache, attend the chunk)",
         "ms": ms, "config": dict(P, S=None, Sq=Sq, Sk=Sk),
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops}}
-    log("prefill chunk Sq=%d over a kept %d-key cache: %.3f ms" % (Sq, Sk, ms))
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_tflops": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                     "algorithmic_flops_per_launch": flops}}
+    log("prefill chunk Sq=%d over a kept %d-key cache: %.3f ms, %.0f GB/s algorithmic (%.1f%% of HBM peak; %.1f%% "
+        "of bf16 MFMA peak)" % (Sq, Sk, ms, gbs, 100 * gbs / HBM_PEAK_GBS, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
     del q, k, v, o, cache, kn, vn, scratch
 
     # non-causal windows (|i - j| against W_p), S=32K
