@@ -561,8 +561,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     // windows applying to |i - j|
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
-    // key tiles of this workgroup's split of the key range: [kt0, kt1)
-    const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
+    // key tiles of this workgroup's split: kt0, kt0 + ks, ... below n_kt.  The
+    // splits take the tiles in turn rather than contiguous ranges, so the
+    // tiles near the queries, whose windows put boundary pairs and more kept
+    // pairs in them and which cost up to several times a far tile, are
+    // spread over all splits.
+    const int kt0 = sp, ks = a.n_ksplit;
 
     // Direct global->LDS loads of tile kt into buffer buf.  Lane l of this
     // wave's n-th 1 KB piece lands at LDS byte piece*1024 + 16 l (lane-linear),
@@ -658,13 +662,13 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
     const unsigned vbase_lane = KT_BYTES + (unsigned)qi * 128;
     const unsigned vz = (unsigned)((swz8(qi) ^ half) << 4);
 
-    if (kt0 < kt1) ATF_TILE_LOAD(kt0, 0, 3);
+    if (kt0 < n_kt) ATF_TILE_LOAD(kt0, 0, 3);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
+    for (int kt = kt0, it = 0; kt < n_kt; kt += ks, ++it) {
+        const int buf = it & 1;
+        const bool more = kt + ks < n_kt;
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * KT;
 
@@ -741,12 +745,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             const int sf = p_t >> 3, zb = p_t - 8 * sf - koff0;
 #pragma unroll
             for (int kp = 0; kp < NB; kp += 2) {
-                if (NB > 2 && kp == 2 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 2);
+                if (NB > 2 && kp == 2 && more) ATF_TILE_LOAD(kt + ks, buf ^ 1, 2);
                 const unsigned char *lv = lt + (kp >> 1) * (D * 128);
                 qk_pair<NSTEP>(sf, lt, kbase_lane + 32u * kp * (CH * 16), kbase_lane + 32u * (kp + 1) * (CH * 16), ky,
                                qf, zb, ones_a, negm_b, sacc[0], sacc[1], pw[0], lsum[0]);
                 // (a one-pair tile takes its values here too)
-                if (kp == 0 && more) ATF_TILE_LOAD(kt + 1, buf ^ 1, NB > 2 ? 1 : 3);
+                if (kp == 0 && more) ATF_TILE_LOAD(kt + ks, buf ^ 1, NB > 2 ? 1 : 3);
                 ATF_BLOCK_RESCALE(0, true)
                 block_pv<NDB>(o, lv, vbase_lane, vz, 0, pw[0]);
                 block_probs(sacc[1], pw[1], lsum[1]);
@@ -758,7 +762,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 8 / kPrefillWaves) void prefill
             continue;
         }
 
-        if (more) ATF_TILE_LOAD(kt + 1, buf ^ 1, 3);
+        if (more) ATF_TILE_LOAD(kt + ks, buf ^ 1, 3);
         int p_lo[NB], p_full[NB];
         bool live[NB];
 #pragma unroll
@@ -1024,8 +1028,12 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const unsigned char *vg = (const unsigned char *)a.vt + (long long)(b * a.Hkv + hk) * a.Sk_pad * (D * 2);
     const int last_key = CAUSAL ? min(a.Sk - 1, q0k + QS - 1) : a.Sk - 1;
     const int n_kt = last_key / KT + 1;
-    // key tiles of this workgroup's split of the key range: [kt0, kt1)
-    const int kt0 = (int)((long long)sp * n_kt / a.n_ksplit), kt1 = (int)((long long)(sp + 1) * n_kt / a.n_ksplit);
+    // key tiles of this workgroup's split: kt0, kt0 + ks, ... below n_kt.  The
+    // splits take the tiles in turn rather than contiguous ranges, so the
+    // tiles near the queries, whose windows put boundary pairs and more kept
+    // pairs in them and which cost up to several times a far tile, are
+    // spread over all splits.
+    const int kt0 = sp, ks = a.n_ksplit;
 
     // Tile loader: piece m (1 KB) of K' lands lane-linear at LDS byte 1024 m +
     // 16 l, i.e. row (1024 m + 16 l) / row_bytes, physical chunk l % CH; the
@@ -1085,13 +1093,13 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const unsigned ksw0 = (unsigned)kswz_sub(krow_t), ksw1 = (unsigned)kswz_sub(krow_t + 8);
     const unsigned vrow_base = KT_BYTES + (unsigned)t * 128;
 
-    if (kt0 < kt1) ATF16_TILE_LOAD(kt0, 0);
+    if (kt0 < n_kt) ATF16_TILE_LOAD(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
-        if (kt + 1 < kt1) ATF16_TILE_LOAD(kt + 1, buf ^ 1);
+    for (int kt = kt0, it = 0; kt < n_kt; kt += ks, ++it) {
+        const int buf = it & 1;
+        if (kt + ks < n_kt) ATF16_TILE_LOAD(kt + ks, buf ^ 1);
         const unsigned char *lt = lds + buf * TILE_BYTES;
         const int j0 = kt * KT;
 
