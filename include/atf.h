@@ -173,7 +173,9 @@ atf_status atf_prefill_attend(const void *q, const void *k, const void *v, void 
  * Workspace bytes with which atf_prefill_chunk may split the key range: the
  * prepared keys and values of atf_prefill_workspace_bytes(B, Hkv, Sk, d,
  * dtype), followed by B*Hq*Sq*n_split rows of d + 2 floats of partials when
- * the planner splits (n_split <= 64).  Equal to atf_prefill_workspace_bytes
+ * the planner splits (n_split <= 64) and, for a split chunk on 16-query waves
+ * (d = 256, or d = 128 with Sq <= 16), from the next 256-byte boundary
+ * B*Hq*Sq*d/2 words of queries rotated once for all splits.  Equal to atf_prefill_workspace_bytes
  * when no split would help (fp32, or a chunk that already fills the GPU).
  * Returns 0 for shapes atf_prefill_chunk rejects.
  */
@@ -223,7 +225,8 @@ atf_status atf_prefill_cache_append(const void *k, const void *v, int32_t B, int
 /*
  * Scratch bytes for atf_prefill_chunk_cached: 256 (the dropped-term counter)
  * plus, when the planner splits the key range, B*Hq*Sq*n_split rows of d + 2
- * floats of partials (n_split <= 64).  0 for rejected shapes.
+ * floats of partials (n_split <= 64) and the rotated queries laid out as in
+ * atf_prefill_chunk_workspace_bytes.  0 for rejected shapes.
  */
 size_t atf_prefill_cached_scratch_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d);
 
@@ -235,7 +238,7 @@ size_t atf_prefill_cached_scratch_bytes(int32_t B, int32_t Hq, int32_t Hkv, int6
  * the same split (the same scratch or workspace size class).  Keys 0 .. Sk - 1
  * must have been appended.  `scratch` (device, >= 256 bytes, 16-byte
  * aligned) takes the counter; with atf_prefill_cached_scratch_bytes(...)
- * bytes or more it also takes the split partials.  Calls that share a
+ * bytes or more it also takes the split partials (and rotated queries).  Calls that share a
  * scratch buffer must be ordered.  Errors: Sq < 1, Sq > Sk or Sk > S_cap is
  * ATF_ERR_INVALID_ARG; a short cache or scratch is ATF_ERR_WORKSPACE; other
  * rules as atf_prefill_chunk.

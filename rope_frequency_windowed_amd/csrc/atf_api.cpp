@@ -148,10 +148,24 @@ size_t pcache_bytes(int32_t B, int32_t Hkv, int64_t S_cap, int32_t d) {
     return 2 * (size_t)B * Hkv * (size_t)padded_keys(S_cap) * d * 2;
 }
 
+// Bytes after the counter (and the prepared keys) that a key-split chunk
+// uses: the splits' partials, then (16x16x32 kernel: d = 256, or d = 128
+// with at most 16 queries) the queries rotated once for all splits, at a
+// 256-byte boundary.
+size_t split_partials_bytes(int32_t B, int32_t Hq, int64_t Sq, int32_t d, int ns) {
+    return (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float);
+}
+bool split_rotates_queries(int64_t Sq, int32_t d, int ns) { return ns > 1 && (d == 256 || (d == 128 && Sq <= 16)); }
+size_t split_extra_bytes(int32_t B, int32_t Hq, int64_t Sq, int32_t d, int ns) {
+    if (ns <= 1) return 0;
+    size_t n = split_partials_bytes(B, Hq, Sq, d, ns);
+    if (split_rotates_queries(Sq, d, ns)) n = (n + 255) / 256 * 256 + (size_t)B * Hq * (size_t)Sq * (d / 2) * 4;
+    return n;
+}
+
 size_t chunk_ws_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d, atf_dtype dtype) {
     const int ns = chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, dtype);
-    const size_t part = ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0;
-    return prefill_ws_bytes(B, Hkv, Sk, d, dtype) + part;
+    return prefill_ws_bytes(B, Hkv, Sk, d, dtype) + split_extra_bytes(B, Hq, Sq, d, ns);
 }
 
 // ---------------------------------------------------------------- decode plan
@@ -298,8 +312,10 @@ atf_status attend_core(const void *q, const void *k, const void *v, void *out, i
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
     window_table_i32(d, rope_base, alpha, a.W);
     theta_table(d, rope_base, a.theta);
-    // the count is per call: clear it (the prepared keys may be reused)
-    hipError_t e = launch_fill_zero_u64(a.counter, s);
+    // the count is per call: clear it (the prepared keys may be reused); a
+    // key-split short chunk clears it in the query-rotation pass instead
+    const bool qrot = dtype == ATF_BF16 && split_rotates_queries(Sq, d, n_ksplit);
+    hipError_t e = qrot ? hipSuccess : launch_fill_zero_u64(a.counter, s);
     if (e != hipSuccess) return ATF_ERR_HIP;
     if (dtype == ATF_F32) {
         // the fp32 kernel rotates raw keys itself: `krot` carries k, `vt` carries v
@@ -319,6 +335,12 @@ atf_status attend_core(const void *q, const void *k, const void *v, void *out, i
         a.n_groups = a.n_qtiles * B * Hkv;
         a.n_ksplit = n_ksplit;
         a.part = n_ksplit > 1 ? part : nullptr;
+        if (qrot) {
+            const size_t off = (split_partials_bytes(B, Hq, Sq, d, n_ksplit) + 255) / 256 * 256;
+            a.qrot = (unsigned *)((char *)part + off);
+            e = launch_prefill_qrot(a, d, s);
+            if (e != hipSuccess) return ATF_ERR_HIP;
+        }
         e = launch_prefill_bf16(a, d, s);
     }
     if (e != hipSuccess) return ATF_ERR_HIP;
@@ -581,7 +603,7 @@ atf_status atf_prefill_cache_append(const void *k, const void *v, int32_t B, int
 size_t atf_prefill_cached_scratch_bytes(int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq, int64_t Sk, int32_t d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sq > Sk || (!supported_d(d))) return 0;
     const int ns = chunk_ksplit(B, Hq, Hkv, Sq, Sk, d, ATF_BF16);
-    return kHeaderBytes + (ns > 1 ? (size_t)B * Hq * (size_t)Sq * ns * (size_t)(d + 2) * sizeof(float) : 0);
+    return kHeaderBytes + split_extra_bytes(B, Hq, Sq, d, ns);
 }
 
 atf_status atf_prefill_chunk_cached(const void *q, void *out, int32_t B, int32_t Hq, int32_t Hkv, int64_t Sq,

@@ -66,6 +66,7 @@ struct AttnArgs {
     int hpack;                        // 1: a work item is one query block of up to 8 heads sharing a kv head
     int narrow;                       // 1: d = 128 on the 16x16x32 kernel (16-query waves)
     float *part;                      // [B*Hq*Sq][n_ksplit][d + 2]  (o..., m, l), n_ksplit > 1 only
+    unsigned *qrot;                   // optional, 16x16x32 kernel: [B*Hq*Sq][d/2] rotated, scaled query pair words
     float scale_log2;                 // log2(e) / sqrt(d)
     int W[kMaxPairs];                 // windows clamped to int32 (kWindowInf = uncut)
     double theta[kMaxPairs];
@@ -131,6 +132,8 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_attend_f32(const AttnArgs &a, int d, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int d, hipStream_t s);
 hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s);
+// rotates the queries into a.qrot and clears a.counter
+hipError_t launch_prefill_qrot(const AttnArgs &a, int d, hipStream_t s);
 // Device address of the current GPU's copy of the library's scratch array
 // (kNoAllocScratchBytes); looked up once per device and kept.  *ptr = NULL
 // when `s` (non-null) belongs to a device other than the current one.

@@ -998,8 +998,17 @@ __global__ __launch_bounds__(kPrefill16Waves * 64, kPrefill16Waves / 4) void pre
     const int kbase_g = 16 * (g >> 1) + 4 * (g & 1);  // key of slot (sb 0, r 0) in a block
 
     // query operand: step s holds pairs 16 s + 4 g + (0..3) of query t, rotated and scaled
+    // (read from a.qrot when the call rotated the queries once beforehand)
     bf16x8_t qf[NSTEP];
-    {
+    if (a.qrot) {
+        const unsigned *qr = a.qrot + ((long long)(b * a.Hq + h) * a.Sq + my_q) * P;
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            u32x4 w = (u32x4){0u, 0u, 0u, 0u};
+            if (q_valid) w = *(const u32x4 *)(qr + 16 * s + 4 * g);
+            qf[s] = __builtin_bit_cast(bf16x8_t, w);
+        }
+    } else {
         const unsigned short *qrow = (const unsigned short *)a.q + ((long long)(b * a.Hq + h) * a.Sq + my_q) * D;
         const long long pos = a.q_pos0 + my_q;
         const float sc = a.scale_log2;
@@ -2372,6 +2381,33 @@ __global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
 
 __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
 
+// Each query row rotated and pre-scaled once, as the pair words of the
+// 16x16x32 kernel's query operand (pair p: (x'_p, y'_p) * log2(e)/sqrt(d) as
+// bf16, x' in the low half), so the key-split workgroups of a short chunk
+// load them instead of each rotating them again; also clears the counter.
+// grid B*Hq*Sq rows, block d/2 (one pair per thread).
+template <int D>
+__global__ __launch_bounds__(D / 2) void prefill_qrot_kernel(AttnArgs a) {
+    constexpr int P = D / 2;
+    const long long row = blockIdx.x;
+    const int i = (int)(row % a.Sq), p = threadIdx.x;
+    if (row == 0 && p == 0) *a.counter = 0ull;
+    const unsigned short *qrow = (const unsigned short *)a.q + row * D;
+    float x, y;
+    if (a.gptj) {
+        const unsigned w = ((const unsigned *)qrow)[p];
+        x = bf_lo(w);
+        y = bf_hi(w);
+    } else {
+        x = __uint_as_float((unsigned)qrow[p] << 16);
+        y = __uint_as_float((unsigned)qrow[p + P] << 16);
+    }
+    float c, sn;
+    rope_cos_sin(a.q_pos0 + i, a.theta[p], c, sn);
+    const float sc = a.scale_log2;
+    a.qrot[row * P + p] = pack_bf((x * c - y * sn) * sc, (y * c + x * sn) * sc);
+}
+
 // The decode queries, rotated once per call at their position (pos0 + S, or
 // pos0 + seq_lens[b] when paged) and scaled by log2(e)/sqrt(d): word p of row
 // b*Hq + h is (x'_p, x'_{p+P}) in bf16, the score MFMA's operand order, so the
@@ -2519,6 +2555,14 @@ hipError_t launch_decode_kcache_bf16(const DecodeArgs &a, int d, hipStream_t s) 
 
 hipError_t launch_fill_zero_u64(unsigned long long *p, hipStream_t s) {
     fill_zero_u64_kernel<<<1, 1, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_qrot(const AttnArgs &a, int d, hipStream_t s) {
+    const unsigned rows = (unsigned)((long long)a.B * a.Hq * a.Sq);
+    if (d == 256) prefill_qrot_kernel<256><<<rows, 128, 0, s>>>(a);
+    else if (d == 128) prefill_qrot_kernel<128><<<rows, 64, 0, s>>>(a);
+    else prefill_qrot_kernel<64><<<rows, 32, 0, s>>>(a);
     return hipGetLastError();
 }
 

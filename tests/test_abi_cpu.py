@@ -151,11 +151,20 @@ def test_workspace_sizes(lib):
     assert atf.atf_decode_workspace_bytes(1, 3, 2, 10, 128) == 0
 
 
+def _split_extra(B, Hq, Sq, d, ns):
+    """Partials of ns splits, then (16x16x32 kernel: d = 256, or d = 128 with
+    at most 16 queries) the rotated queries at a 256-byte boundary."""
+    part = B * Hq * Sq * ns * (d + 2) * 4
+    if d == 256 or Sq <= 16:
+        part = (part + 255) // 256 * 256 + B * Hq * Sq * (d // 2) * 4
+    return part
+
+
 def test_chunk_workspace_sizes(lib):
     pre = atf.atf_prefill_workspace_bytes(1, 4, 32768, 128, atf.ATF_BF16)
     # 16 queries, 4 heads: one query tile per head, 512 // 4 = 128 capped at 64 splits
     assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 16, 32768, 128, atf.ATF_BF16) == \
-        pre + 4 * 16 * 64 * 130 * 4
+        pre + _split_extra(1, 4, 16, 128, 64)
     # at most Sk / 256 splits (two 128-key tiles each)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 4, 4, 17, 1000, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 4 * 17 * 3 * 130 * 4
@@ -168,7 +177,7 @@ def test_chunk_workspace_sizes(lib):
     # 7 heads per kv head, 16 queries: head-packed work items (one per kv head)
     # leave 4 workgroups with work, so 64 splits; unpacked it would be 28 (18 splits)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 131072, 128, atf.ATF_BF16) == \
-        atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + 28 * 16 * 64 * 130 * 4
+        atf.atf_prefill_workspace_bytes(1, 4, 131072, 128, atf.ATF_BF16) + _split_extra(1, 28, 16, 128, 64)
     # 4096 queries after 126976 cached tokens: 448 query-tile workgroups fill
     # 1.75 rounds of 256; four splits make 7 full rounds
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 4096, 131072, 128, atf.ATF_BF16) == \
@@ -179,12 +188,12 @@ def test_chunk_workspace_sizes(lib):
     # at most 16 queries (d = 128): 64-key tiles of the 16x16x32 kernel, so
     # Sk = 1000 allows 7 splits of two tiles (128-key tiles would allow 3)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 16, 1000, 128, atf.ATF_BF16) == \
-        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 28 * 16 * 7 * 130 * 4
+        atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + _split_extra(1, 28, 16, 128, 7)
     assert atf.atf_prefill_chunk_workspace_bytes(1, 28, 4, 17, 1000, 128, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 4, 1000, 128, atf.ATF_BF16) + 28 * 17 * 3 * 130 * 4
     # d = 256: 64-key tiles, 128-query tiles
     assert atf.atf_prefill_chunk_workspace_bytes(1, 2, 1, 100, 1500, 256, atf.ATF_BF16) == \
-        atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + 2 * 100 * 11 * 258 * 4
+        atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + _split_extra(1, 2, 100, 256, 11)
     for bad in ((1, 3, 2, 16, 100, 128), (1, 4, 4, 0, 100, 128), (1, 4, 4, 101, 100, 128),
                 (1, 4, 4, 16, 100, 96)):
         assert atf.atf_prefill_chunk_workspace_bytes(*bad, atf.ATF_BF16) == 0
@@ -424,8 +433,10 @@ def test_prefill_cache_sizes(lib):
     assert atf.atf_prefill_cache_bytes(2, 1, 128, 64) == 2 * 2 * 128 * 64 * 2
     assert atf.atf_prefill_cache_bytes(1, 4, 3000, 96) == 0
     assert atf.atf_prefill_cache_bytes(1, 4, 0, 128) == 0
-    # scratch: counter, plus the partials of the same split the chunk call plans
-    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 16, 131072, 128) == 256 + 28 * 16 * 64 * 130 * 4
+    # scratch: counter, plus the partials (and rotated queries) of the same
+    # split the chunk call plans
+    assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 16, 131072, 128) == 256 + _split_extra(1, 28, 16, 128, 64)
+    assert _split_extra(1, 28, 16, 128, 64) == 28 * 16 * 64 * 130 * 4 + 28 * 16 * 64 * 4
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 32768, 32768, 128) == 256
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 4, 17, 16, 128) == 0
     assert atf.atf_prefill_cached_scratch_bytes(1, 28, 3, 16, 100, 128) == 0
