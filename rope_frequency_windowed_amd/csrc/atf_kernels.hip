@@ -2371,12 +2371,79 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // Prefill split over the key range: grid B*Hq*Sq (one query row each), block D.
+// One output row of a key-split prefill, one thread per dim walking every
+// split (few splits: chunks of many queries).
 template <int D>
 __global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
     const long long row = blockIdx.x;
     const int c = threadIdx.x;
     const float *pr = a.part + row * a.n_ksplit * (D + 2);
     ((__bf16 *)a.out)[row * D + c] = (__bf16)combine_row<D>(pr, a.n_ksplit, c);
+}
+
+// One output row of a key-split prefill with many splits: kCombineGroups groups of D threads
+// each merge every kCombineGroups-th split of dim c with a running maximum
+// (one pass over the partials, four loads in flight per thread), then the
+// groups' (max, numerator, denominator) meet in LDS.  Many splits and few rows
+// (a short chunk: 64 splits, 448 rows) keep more loads in flight this way
+// than one thread per dim walking all splits twice.
+constexpr int kCombineGroups = 4;
+template <int D>
+__global__ __launch_bounds__(D * kCombineGroups) void prefill_combine_wide_kernel(AttnArgs a) {
+    constexpr int G = kCombineGroups, U = 4;
+    __shared__ float red[3][G][D];
+    const long long row = blockIdx.x;
+    const int c = threadIdx.x % D, gr = threadIdx.x / D;
+    const int ns = a.n_ksplit;
+    const float *pr = a.part + row * ns * (D + 2);
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = gr; s0 < ns; s0 += G * U) {
+        float m[U], o[U], l[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * G;
+            m[u] = -INFINITY;
+            o[u] = l[u] = 0.f;
+            if (s < ns) {
+                const float *ps = pr + s * (D + 2);
+                m[u] = ps[D];
+                o[u] = ps[c];
+                l[u] = ps[D + 1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (m[u] == -INFINITY) continue;  // a split with none of the row's mass (or past the end)
+            if (m[u] > M) {
+                const float r = fast_exp2(M - m[u]);  // 0 while M is -inf
+                num *= r;
+                den *= r;
+                M = m[u];
+            }
+            const float f = fast_exp2(m[u] - M);
+            num += f * o[u];
+            den += f * l[u];
+        }
+    }
+    red[0][gr][c] = M;
+    red[1][gr][c] = num;
+    red[2][gr][c] = den;
+    __syncthreads();
+    if (gr == 0) {
+        float Mt = red[0][0][c];
+#pragma unroll
+        for (int g = 1; g < G; ++g) Mt = fmaxf(Mt, red[0][g][c]);
+        float nt = 0.f, dt = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float mg = red[0][g][c];
+            if (mg == -INFINITY) continue;
+            const float f = fast_exp2(mg - Mt);
+            nt += f * red[1][g][c];
+            dt += f * red[2][g][c];
+        }
+        ((__bf16 *)a.out)[row * D + c] = (__bf16)(nt / dt);
+    }
 }
 
 __global__ void fill_zero_u64_kernel(unsigned long long *p) { *p = 0ull; }
@@ -2472,9 +2539,15 @@ hipError_t launch_prefill_bf16(const AttnArgs &a, int d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_ksplit <= 1) return e;
     const unsigned rows = (unsigned)((long long)a.B * a.Hq * a.Sq);
-    if (d == 256) prefill_combine_kernel<256><<<rows, 256, 0, s>>>(a);
-    else if (d == 128) prefill_combine_kernel<128><<<rows, 128, 0, s>>>(a);
-    else prefill_combine_kernel<64><<<rows, 64, 0, s>>>(a);
+    if (a.n_ksplit >= 4 * kCombineGroups) {
+        if (d == 256) prefill_combine_wide_kernel<256><<<rows, 256 * kCombineGroups, 0, s>>>(a);
+        else if (d == 128) prefill_combine_wide_kernel<128><<<rows, 128 * kCombineGroups, 0, s>>>(a);
+        else prefill_combine_wide_kernel<64><<<rows, 64 * kCombineGroups, 0, s>>>(a);
+    } else {
+        if (d == 256) prefill_combine_kernel<256><<<rows, 256, 0, s>>>(a);
+        else if (d == 128) prefill_combine_kernel<128><<<rows, 128, 0, s>>>(a);
+        else prefill_combine_kernel<64><<<rows, 64, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
