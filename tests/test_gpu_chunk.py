@@ -272,3 +272,27 @@ def test_chunk_full_round_split(env):
     ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=Sk - Sq, k_pos0=0)
     check_bf16(out.float().cpu().numpy(), ref, None, "chunk full-round split")
     assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
+
+
+@pytest.mark.parametrize("d,Sq,layout,pos0", [(128, 16, "gptj", 0), (128, 5, "gptj", 1 << 20),
+                                              (256, 16, "gptj", 12345), (256, 40, "neox", 1 << 22)])
+def test_chunk_split_rotated_queries(env, d, Sq, layout, pos0):
+    """Key-split chunks on 16-query waves rotate their queries once, in a pass
+    of their own, for all splits: both rotary layouts and shifted positions
+    against the oracle, with the exact dropped-term count."""
+    torch, oracle, atf, inputs = env
+    B, Hq, Hkv, Sk, base, alpha = 2, 8, 2, 2500, 1e6, 1.0
+    log("case: chunk split rotated queries d=%d Sq=%d %s pos0=%d" % (d, Sq, layout, pos0))
+    dev = torch.device("cuda:0")
+    assert atf.atf_prefill_chunk_workspace_bytes(B, Hq, Hkv, Sq, Sk, d, atf.ATF_BF16) > \
+        atf.atf_prefill_workspace_bytes(B, Hkv, Sk, d, atf.ATF_BF16)
+    q, k, v = inputs.make_qkv(B, Hq, Hkv, Sq, Sk, d, dtype=torch.bfloat16, device=dev)
+    out, skipped = atf.atf_prefill_chunk(q, k, v, rope_base=base, alpha=alpha, pos0=pos0, rope_layout=layout,
+                                         return_skipped=True)
+    torch.cuda.synchronize()
+    ref, ref_skipped = oracle.attention(q, k, v, base=base, alpha=alpha, q_pos0=pos0 + Sk - Sq, k_pos0=pos0,
+                                        layout=layout)
+    dense, _ = oracle.attention(q, k, v, base=base, alpha=math.inf, q_pos0=pos0 + Sk - Sq, k_pos0=pos0,
+                                layout=layout)
+    check_bf16(out.float().cpu().numpy(), ref, dense, "chunk split rotated queries d=%d Sq=%d %s" % (d, Sq, layout))
+    assert skipped == ref_skipped == B * Hq * chunk_closed_form(atf, Sq, Sk, d, base, alpha)
