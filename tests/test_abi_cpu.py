@@ -155,7 +155,7 @@ def _split_extra(B, Hq, Sq, d, ns):
     """Partials of ns splits, then (16x16x32 kernel: d = 256, or d = 128 with
     at most 16 queries) the rotated queries at a 256-byte boundary."""
     part = B * Hq * Sq * ns * (d + 2) * 4
-    if d == 256 or Sq <= 16:
+    if d == 256 or (d == 128 and Sq <= 16):
         part = (part + 255) // 256 * 256 + B * Hq * Sq * (d // 2) * 4
     return part
 
