@@ -194,6 +194,12 @@ def test_chunk_workspace_sizes(lib):
     # d = 256: 64-key tiles, 128-query tiles
     assert atf.atf_prefill_chunk_workspace_bytes(1, 2, 1, 100, 1500, 256, atf.ATF_BF16) == \
         atf.atf_prefill_workspace_bytes(1, 1, 1500, 256, atf.ATF_BF16) + _split_extra(1, 2, 100, 256, 11)
+    # d = 64 short chunks run on the 32x32 kernel, which rotates its own
+    # queries: partials only (a whole number of split rows, at most 64 splits)
+    extra = atf.atf_prefill_chunk_workspace_bytes(1, 4, 2, 16, 3000, 64, atf.ATF_BF16) - \
+        atf.atf_prefill_workspace_bytes(1, 2, 3000, 64, atf.ATF_BF16)
+    row = 4 * 16 * 66 * 4
+    assert extra > 0 and extra % row == 0 and 1 < extra // row <= 64
     for bad in ((1, 3, 2, 16, 100, 128), (1, 4, 4, 0, 100, 128), (1, 4, 4, 101, 100, 128),
                 (1, 4, 4, 16, 100, 96)):
         assert atf.atf_prefill_chunk_workspace_bytes(*bad, atf.ATF_BF16) == 0
