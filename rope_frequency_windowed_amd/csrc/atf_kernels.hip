@@ -124,16 +124,6 @@ __device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
     return v;
 }
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
 
 // LDS swizzles.  A 64-lane ds_read_b128 is served 8 or 16 lanes per pass;
 // these make the 8 and the 16 rows read in one pass land in distinct bank
@@ -153,7 +143,7 @@ constexpr int kswz_rows() { return (CH >= 16) ? 16 : 8; }  // period of kswz in 
 // Keys [k_begin, k_end) come from source rows 0 .. k_end - k_begin - 1; keys
 // past k_end are cleared, keys before k_begin (the first tile of an append
 // that does not start on a tile) are kept.
-// grid (number of 64-key tiles from tile0, B*Hkv), block 256.
+// grid (number of 64-key tiles from tile0, B*Hkv, d/32: 16 pairs each), block 256.
 // ============================================================================
 
 // Key held at position `pos` (0..15) of a 16-key group of a value tile.
@@ -165,18 +155,18 @@ __device__ inline int vt_key_of_pos(int pos) {
 template <int D>
 __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
     constexpr int P = D / 2;
-    constexpr int PPT = P / 4;  // pairs per thread (16 or 8)
-    const int tile = a.tile0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+    constexpr int PPT = 4;  // pairs per thread: block z rotates pairs 16 z .. 16 z + 15 of the tile's 64 keys
+    const int tile = a.tile0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x, z = blockIdx.z;
     // source rows: key j is row j - k_begin
     const unsigned short *k = (const unsigned short *)a.k + (long long)bh * a.src_rows * D;
     const unsigned short *v = (const unsigned short *)a.v + (long long)bh * a.src_rows * D;
     unsigned *kr = (unsigned *)a.krot + (long long)bh * a.S_pad * P;
     unsigned short *vt = (unsigned short *)a.vt + ((long long)bh * (a.S_pad / kKeyTile) + tile) * (D * kKeyTile);
 
-    if (a.counter && blockIdx.x == 0 && bh == 0 && t == 0) *a.counter = 0ull;
+    if (a.counter && blockIdx.x == 0 && bh == 0 && z == 0 && t == 0) *a.counter = 0ull;
 
     {  // keys
-        const int row = t >> 2, p0 = (t & 3) * PPT;
+        const int row = t >> 2, p0 = 16 * z + (t & 3) * PPT;
         const int j = tile * kKeyTile + row;
         union { u32x4 v[PPT / 4]; unsigned w[PPT]; } res;
         if (j >= a.k_begin && j < a.k_end) {
@@ -203,6 +193,7 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(PrepArgs a) {
         }
     }
 
+    if (z != 0) return;  // the values of the tile: block z = 0
     {  // values: tile [64][D] -> LDS -> [D][64] with the in-group key permutation
         constexpr int LD = D + 8;  // padded LDS row (ushort)
         __shared__ unsigned short vs[kKeyTile * LD];
@@ -2370,9 +2361,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     ((__bf16 *)a.out)[(long long)row * D + c] = (__bf16)combine_row<D>(pr, ns, c);
 }
 
-// Prefill split over the key range: grid B*Hq*Sq (one query row each), block D.
-// One output row of a key-split prefill, one thread per dim walking every
-// split (few splits: chunks of many queries).
+// Merge of a key-split prefill: grid B*Hq*Sq (one query row each), block D,
+// one thread per dim walking every split (few splits: chunks of many
+// queries).
 template <int D>
 __global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
     const long long row = blockIdx.x;
@@ -2381,12 +2372,12 @@ __global__ __launch_bounds__(D) void prefill_combine_kernel(AttnArgs a) {
     ((__bf16 *)a.out)[row * D + c] = (__bf16)combine_row<D>(pr, a.n_ksplit, c);
 }
 
-// One output row of a key-split prefill with many splits: kCombineGroups groups of D threads
-// each merge every kCombineGroups-th split of dim c with a running maximum
-// (one pass over the partials, four loads in flight per thread), then the
-// groups' (max, numerator, denominator) meet in LDS.  Many splits and few rows
-// (a short chunk: 64 splits, 448 rows) keep more loads in flight this way
-// than one thread per dim walking all splits twice.
+// The same merge with many splits: grid B*Hq*Sq, block kCombineGroups * D.
+// Each group of D threads merges every kCombineGroups-th split of dim c with
+// a running maximum (one pass over the partials, four loads in flight per
+// thread), then the groups' (max, numerator, denominator) meet in LDS.  Many
+// splits and few rows (a short chunk: 64 splits, 448 rows) keep more loads in
+// flight this way than one thread per dim walking all splits twice.
 constexpr int kCombineGroups = 4;
 template <int D>
 __global__ __launch_bounds__(D * kCombineGroups) void prefill_combine_wide_kernel(AttnArgs a) {
@@ -2508,7 +2499,9 @@ void launch_decode_qrot(const DecodeArgs &a, int d, hipStream_t s) {
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_prep_bf16(const PrepArgs &a, int d, hipStream_t s) {
-    dim3 grid((unsigned)a.n_tiles, (unsigned)(a.B * a.Hkv));
+    // one block per (tile, b x kv head, 16 pairs): an append of a few keys
+    // rotates them across d / 32 blocks instead of one
+    dim3 grid((unsigned)a.n_tiles, (unsigned)(a.B * a.Hkv), (unsigned)(d / 32));
     if (d == 256) prep_bf16_kernel<256><<<grid, 256, 0, s>>>(a);
     else if (d == 128) prep_bf16_kernel<128><<<grid, 256, 0, s>>>(a);
     else prep_bf16_kernel<64><<<grid, 256, 0, s>>>(a);
