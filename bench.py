@@ -43,6 +43,7 @@ KCACHE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kcache_kv262144_co
 PAGED_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_paged_kv262144_counters.txt")
 GPTJ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_gptj_kv262144_counters.txt")
 D256_DECODE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_d256_kv65536_counters.txt")
+D256_PREFILL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill16_d256_s32768_counters.txt")
 SQ_COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_attend_s131072_sq_counters.txt")
 N_SIMD, CLOCK_HZ = 1024, 2.4e9   # MI355X: 256 CUs x 4 SIMDs, peak engine clock
 
@@ -404,7 +405,8 @@ def variant_legs(atf, torch, make_qkv, dev, stream, steps):
                            "config": P,
                            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                                        "algorithmic_flops_per_launch": flops}}
+                                        "algorithmic_flops_per_launch": flops,
+                                        "traffic": read_traffic(D256_PREFILL_COUNTERS_FILE)}}
     log("prefill d=256 S=%d: attend %.3f ms, %.1f TFLOP/s (%.1f%% of bf16 peak)"
         % (P["S"], ms, tf, 100 * tf / MFMA_BF16_PEAK_TFLOPS))
     del q, k, v, o, ws
